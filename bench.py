@@ -1,0 +1,218 @@
+"""Benchmark of the SVDQuant W4A4 linear on one MI355X.
+
+One step = the whole hot path of one linear layer on one batch: the activation kernel
+(smoothing, INT4 group quantization, fused low-rank down-projection) followed by the W4A4
+GEMM (per-group dequantization, low-rank up-projection, bias), for the DiT attention
+projection at 1024x1024 image scale: M = 4096 tokens, K = N = 3072, rank 32, INT4 groups
+of 64, bf16 bias, bf16 output.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is TOPS of the linear, counting 2MNK + 2MNr + 2MKr
+operations per step (the low-rank branch's flops included, the dense bf16 work the method
+avoids not counted), with every input already in HBM.  Inputs rotate through enough copies
+(> 256 MB) that each step reads activations and weights from HBM, not from the MI355X's
+256 MB last-level cache.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+
+M, K, N, R = 4096, 3072, 3072, 32
+WORKLOAD = "attn_4096x3072x3072_r32"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=10,
+                    help="rotating input sets (each ~30 MB) to defeat the last-level cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="token rows of the workload the CPU oracle baseline runs")
+    return ap.parse_args()
+
+
+def make_inputs(copies):
+    """Synthetic inputs of the attention-projection workload, on the GPU.
+
+    Activations: the workload's draw (bf16 N(0,1), 31 outlier channels x50).  Smoothing
+    factors from the activation and weight column maxima.  The 4-bit residual weights are
+    produced by this library's own activation kernel from a synthetic bf16 residual (the
+    GEMM's speed does not depend on the code values).  Low-rank factors: bf16 N(0, 0.02).
+    """
+    import torch
+    import synth
+    import bit_diffusion_amd as bd
+
+    wl = synth.WORKLOADS[1]
+    d = synth.draw(wl)
+    xb = d.x_bf16
+    xmax = np.abs(synth.bf16_bits_to_f32(xb)).max(axis=0).astype(np.float64)
+    wmax = np.abs(d.w).max(axis=0)
+    lam = np.sqrt(np.where((xmax > 0) & (wmax > 0), xmax / np.maximum(wmax, 1e-30), 1.0))
+    smooth_inv = (1.0 / lam).astype(np.float32)
+    rng = np.random.default_rng(7)
+    dev = "cuda:0"
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    si = torch.from_numpy(smooth_inv).to(dev)
+    ones = torch.ones(K, dtype=torch.float32, device=dev)
+    resid = synth.f32_to_bf16_bits((d.w * lam[None, :]).astype(np.float32))
+    sets = []
+    cfg_w = bd.LayerCfg.make(K, N, 0)
+    for c in range(copies):
+        x = t16(xb) if c == 0 else t16(np.roll(xb, c, axis=0))
+        rt = t16(resid if c == 0 else np.roll(resid, c, axis=0))
+        wc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        ws = torch.empty((N, K // 64), dtype=torch.float32, device=dev)
+        bd.svdq_quantize_act(cfg_w, N, rt, ones, None, 1.0, wc, ws, None)
+        del rt
+        s = dict(
+            x=x, wc=wc, ws=ws,
+            l1=t16(synth.random_bf16(rng, (R, K), 0.02)),
+            l2=t16(synth.random_bf16(rng, (N, R), 0.02)),
+            bias=t16(d.bias_bf16),
+            codes=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+            scales=torch.empty((M, K // 64), dtype=torch.float32, device=dev),
+            lora=torch.empty((M, R), dtype=torch.int16, device=dev),
+            out=torch.empty((M, N), dtype=torch.int16, device=dev),
+        )
+        sets.append(s)
+    torch.cuda.synchronize()
+    return si, sets, d
+
+
+def cpu_baseline(rows):
+    """The CPU oracle (single thread, as it stands) on the first `rows` token rows of the
+    same workload: activation stage + GEMM with the low-rank branch and bias."""
+    import oracle
+    import synth
+
+    wl = synth.WORKLOADS[1]
+    d = synth.draw(wl)
+    rng = np.random.default_rng(7)
+    xb = np.ascontiguousarray(d.x_bf16[:rows])
+    si = np.ones(K, np.float32)
+    l1 = synth.random_bf16(rng, (R, K), 0.02)
+    l2 = synth.random_bf16(rng, (N, R), 0.02)
+    wc = synth.random_packed_nibbles(rng, N, K)
+    ws = rng.uniform(0.001, 0.1, (N, K // 64)).astype(np.float32)
+    oracle.lib()
+    t0 = time.perf_counter()
+    c, s, lo = oracle.quant_act_int4(xb, si, l1)
+    oracle.gemm_w4a4_int4(c, s, wc, ws, lo, l2, d.bias_bf16)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * N * K + 2.0 * rows * N * R + 2.0 * rows * K * R
+    return dict(value=ops / dt / 1e12, unit="TOPS", cores=1, kind="oracle",
+                sample=f"{rows} of {M} token rows, full K and N, single-threaded C oracle, "
+                       f"{dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the linear "
+              "shards over tokens with no communication, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_diffusion_amd as bd
+
+    assert bd.svdq_check_device(0) == bd.SVDQ_OK, bd.svdq_last_error()
+    si, sets, _ = make_inputs(args.copies)
+    cfg = bd.LayerCfg.make(K, N, R)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(s):
+        bd.svdq_quantize_act(cfg, M, s["x"], si, s["l1"], 1.0, s["codes"], s["scales"],
+                             s["lora"], sp)
+        bd.svdq_gemm_w4a4(cfg, M, s["codes"], s["scales"], 1.0, s["wc"], s["ws"], 1.0,
+                          s["lora"], s["l2"], s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16,
+                          s["out"], sp)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel timing (events between the two launches of each step)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        evs[3 * i].record(stream)
+        bd.svdq_quantize_act(cfg, M, s["x"], si, s["l1"], 1.0, s["codes"], s["scales"],
+                             s["lora"], sp)
+        evs[3 * i + 1].record(stream)
+        bd.svdq_gemm_w4a4(cfg, M, s["codes"], s["scales"], 1.0, s["wc"], s["ws"], 1.0,
+                          s["lora"], s["l2"], s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16,
+                          s["out"], sp)
+        evs[3 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    t_q = np.array([evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(args.steps)])
+    t_g = np.array([evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(args.steps)])
+
+    ops_gemm = 2.0 * M * N * K + 2.0 * M * N * R
+    ops_total = ops_gemm + 2.0 * M * K * R
+    value = ops_total / (ms_step * 1e-3) / 1e12
+    gemm_tops = ops_gemm / (t_g.mean() * 1e-3) / 1e12
+    quant_bytes = M * K * 2 + K * 4 + R * K * 2 + M * K // 2 + M * (K // 64) * 4 + M * R * 2
+    quant_gbs = quant_bytes / (t_q.mean() * 1e-3) / 1e9
+
+    out = {
+        "metric": "W4A4+low-rank r32 linear TOPS @4096x3072x3072; % of int8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "M": M, "K": K, "N": N, "rank": R, "group": 64,
+                   "out_dtype": "bf16", "bias": True, "pct_of_int8_peak":
+                   round(100 * value / INT8_PEAK_TOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": None, "kernel": "svdq_gemm_w4a4 (int4)",
+                     "ms_per_launch": round(float(t_g.mean()), 5)},
+        "kernels": {
+            "quantize_act_ms": round(float(t_q.mean()), 5),
+            "quantize_act_GBs": round(quant_gbs, 1),
+            "quantize_act_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+            "gemm_ms": round(float(t_g.mean()), 5),
+            "gemm_TOPS": round(gemm_tops, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,91 @@
+"""bit_diffusion_amd -- MI355X (gfx950) SVDQuant W4A4 / AWQ W4A16 linear layers.
+
+Thin Python binding of the C ABI in include/svdq.h (libsvdq.so, built in-tree by
+``python -m bit_diffusion_amd.build``).  Functions keep the C names and argument order;
+they only marshal arguments: torch tensors become device pointers, the stream defaults to
+torch's current stream, and a non-OK status raises SvdqError with the library's message.
+Every computation runs in the library's HIP kernels; there is no fallback path.
+"""
+import ctypes
+import os
+
+from . import _abi
+from ._abi import (SVDQ_OK, SVDQ_ERR_INVALID_ARG, SVDQ_ERR_UNSUPPORTED_DEVICE,  # noqa: F401
+                   SVDQ_ERR_UNSUPPORTED_CONFIG, SVDQ_ERR_LAUNCH, SVDQ_PREC_INT4, SVDQ_PREC_NVFP4,
+                   SVDQ_DT_F32, SVDQ_DT_BF16, SVDQ_ACT_NONE, SVDQ_ACT_GELU_TANH, LayerCfg,
+                   SvdqError, lib, LIB_PATH)
+
+__all__ = [
+    "svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_device",
+    "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
+    "SvdqError", "lib", "LIB_PATH",
+]
+
+
+def _ptr(t):
+    """Device/host address of a tensor (or an int address, or None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status):
+    if status != SVDQ_OK:
+        raise SvdqError(status, svdq_last_error())
+    return status
+
+
+def svdq_quantize_act(cfg, M, x, smooth_inv, l1, act_global_scale, act_codes, act_scales,
+                      lora_act, stream=None):
+    L = lib()
+    return _check(L.svdq_quantize_act(ctypes.byref(cfg), int(M), _ptr(x), _ptr(smooth_inv),
+                                      _ptr(l1), float(act_global_scale), _ptr(act_codes),
+                                      _ptr(act_scales), _ptr(lora_act), _stream(stream)))
+
+
+def svdq_gemm_w4a4(cfg, M, act_codes, act_scales, act_global_scale, wgt_codes, wgt_scales,
+                   wgt_global_scale, lora_act, l2, bias, act, out_dtype, out, stream=None):
+    L = lib()
+    return _check(L.svdq_gemm_w4a4(ctypes.byref(cfg), int(M), _ptr(act_codes), _ptr(act_scales),
+                                   float(act_global_scale), _ptr(wgt_codes), _ptr(wgt_scales),
+                                   float(wgt_global_scale), _ptr(lora_act), _ptr(l2), _ptr(bias),
+                                   int(act), int(out_dtype), _ptr(out), _stream(stream)))
+
+
+def awq_gemm_w4a16(M, K, N, group_size, x, qweight, scales, zeros, bias, out_dtype, out,
+                   stream=None):
+    L = lib()
+    return _check(L.awq_gemm_w4a16(int(M), int(K), int(N), int(group_size), _ptr(x),
+                                   _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(bias),
+                                   int(out_dtype), _ptr(out), _stream(stream)))
+
+
+def svdq_check_device(device=0):
+    return lib().svdq_check_device(int(device))
+
+
+def svdq_check_arch(name):
+    return lib().svdq_check_arch(name.encode() if isinstance(name, str) else name)
+
+
+def svdq_status_string(status):
+    return lib().svdq_status_string(int(status)).decode()
+
+
+def svdq_last_error():
+    return lib().svdq_last_error().decode()
+
+
+def svdq_version():
+    return lib().svdq_version()

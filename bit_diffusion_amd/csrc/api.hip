@@ -1,0 +1,231 @@
+// api.hip -- the extern "C" boundary of libsvdq: argument validation, the device
+// capability check and dispatch to the gfx950 kernels.  Declarations and the contract of
+// every entry point are in include/svdq.h.
+//
+// The capability check follows the pages' rule that an unsupported GPU must fail loudly
+// and never return wrong results (page "Hugging Face 把 Nunchaku 4-bit Diffusion 接到
+// Diffusers", 技术细节 3; page "Nunchaku Lite: 4-битная генерация ...", "Какое железо и
+// модели поддержаны"): every compute entry point checks that the current device is gfx950.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/svdq.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+svdq_status fail(svdq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+svdq_status fail(svdq_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+bool arch_is_gfx950(const char* name) {
+    return std::strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':');
+}
+
+svdq_status check_device_ordinal(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(SVDQ_ERR_INVALID_ARG, "device ordinal %d out of range", dev);
+    int s = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (s == 0) {
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(SVDQ_ERR_INVALID_ARG, "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
+        s = arch_is_gfx950(prop.gcnArchName) ? 1 : 2;
+        g_dev_state[dev].store(s, std::memory_order_relaxed);
+        if (s == 2)
+            return fail(SVDQ_ERR_UNSUPPORTED_DEVICE,
+                        "device %d is %s; this library's 4-bit kernels are built for gfx950 only",
+                        dev, prop.gcnArchName);
+    }
+    if (s == 2)
+        return fail(SVDQ_ERR_UNSUPPORTED_DEVICE,
+                    "device %d is not gfx950; this library's 4-bit kernels are built for gfx950 only",
+                    dev);
+    return SVDQ_OK;
+}
+
+svdq_status check_current_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SVDQ_ERR_UNSUPPORTED_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    return check_device_ordinal(dev);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+svdq_status check_ptr(const void* p, const char* name, size_t align) {
+    if (p == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(SVDQ_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+    return SVDQ_OK;
+}
+
+svdq_status check_cfg(const svdq_layer_cfg* cfg) {
+    if (cfg == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "cfg is NULL");
+    if (cfg->precision != SVDQ_PREC_INT4 && cfg->precision != SVDQ_PREC_NVFP4)
+        return fail(SVDQ_ERR_INVALID_ARG, "precision %d is neither INT4 (0) nor NVFP4 (1)", cfg->precision);
+    if (cfg->in_features <= 0 || cfg->in_features % 64 != 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "in_features %d must be a positive multiple of 64", cfg->in_features);
+    if (cfg->out_features <= 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "out_features %d must be positive", cfg->out_features);
+    const int want_g = cfg->precision == SVDQ_PREC_INT4 ? 64 : 16;
+    if (cfg->group_size != want_g)
+        return fail(SVDQ_ERR_INVALID_ARG, "group_size %d: %s requires %d", cfg->group_size,
+                    cfg->precision == SVDQ_PREC_INT4 ? "INT4" : "NVFP4", want_g);
+    if (cfg->rank < 0 || cfg->rank % 16 != 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "rank %d must be 0 or a positive multiple of 16", cfg->rank);
+    if (cfg->rank > 128)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "rank %d exceeds the supported maximum 128", cfg->rank);
+    return SVDQ_OK;
+}
+
+svdq_status check_global_scale(float s, const char* name) {
+    if (!(std::isfinite(s) && s > 0.0f))
+        return fail(SVDQ_ERR_INVALID_ARG, "%s = %g must be finite and positive", name, (double)s);
+    return SVDQ_OK;
+}
+
+svdq_status after_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SVDQ_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    return SVDQ_OK;
+}
+
+#define SVDQ_TRY(expr)                     \
+    do {                                   \
+        svdq_status _s = (expr);           \
+        if (_s != SVDQ_OK) return _s;      \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_quantize_act(const svdq_layer_cfg* cfg, int64_t M, const void* x,
+                              const float* smooth_inv, const void* l1, float act_global_scale,
+                              void* act_codes, void* act_scales, void* lora_act,
+                              svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    const bool nvfp4 = cfg->precision == SVDQ_PREC_NVFP4;
+    SVDQ_TRY(check_ptr(x, "x", 16));
+    SVDQ_TRY(check_ptr(smooth_inv, "smooth_inv", 16));
+    SVDQ_TRY(check_ptr(act_codes, "act_codes", 16));
+    SVDQ_TRY(check_ptr(act_scales, "act_scales", nvfp4 ? 1 : 4));
+    if (cfg->rank > 0) {
+        SVDQ_TRY(check_ptr(l1, "l1", 16));
+        SVDQ_TRY(check_ptr(lora_act, "lora_act", 16));
+    }
+    if (nvfp4) SVDQ_TRY(check_global_scale(act_global_scale, "act_global_scale"));
+    if (M > (int64_t)65535 * 16 * 1024)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
+    SVDQ_TRY(check_current_device());
+    if (M == 0) return SVDQ_OK;
+    svdq::QuantArgs a{M, cfg->in_features, cfg->rank, nvfp4, x, smooth_inv, l1, act_global_scale,
+                      act_codes, act_scales, lora_act};
+    svdq::launch_quantize_act(a, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_quantize_act");
+}
+
+svdq_status svdq_gemm_w4a4(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
+                           const void* act_scales, float act_global_scale, const void* wgt_codes,
+                           const void* wgt_scales, float wgt_global_scale, const void* lora_act,
+                           const void* l2, const void* bias, int32_t act, int32_t out_dtype,
+                           void* out, svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    const bool nvfp4 = cfg->precision == SVDQ_PREC_NVFP4;
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
+        return fail(SVDQ_ERR_INVALID_ARG, "act %d is not a svdq_act value", act);
+    if (out_dtype != SVDQ_DT_F32 && out_dtype != SVDQ_DT_BF16)
+        return fail(SVDQ_ERR_INVALID_ARG, "out_dtype %d is not a svdq_dtype value", out_dtype);
+    SVDQ_TRY(check_ptr(act_codes, "act_codes", 16));
+    SVDQ_TRY(check_ptr(act_scales, "act_scales", nvfp4 ? 1 : 4));
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", 16));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", nvfp4 ? 1 : 4));
+    SVDQ_TRY(check_ptr(out, "out", out_dtype == SVDQ_DT_F32 ? 4 : 2));
+    if (cfg->rank > 0) {
+        SVDQ_TRY(check_ptr(lora_act, "lora_act", 16));
+        SVDQ_TRY(check_ptr(l2, "l2", 16));
+    }
+    if (bias != nullptr && !aligned(bias, 2)) return fail(SVDQ_ERR_INVALID_ARG, "bias is not 2-byte aligned");
+    if (nvfp4) {
+        SVDQ_TRY(check_global_scale(act_global_scale, "act_global_scale"));
+        SVDQ_TRY(check_global_scale(wgt_global_scale, "wgt_global_scale"));
+    }
+    if ((M + 127) / 128 > 65535)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
+    SVDQ_TRY(check_current_device());
+    if (M == 0) return SVDQ_OK;
+    svdq::GemmArgs a{M, cfg->out_features, cfg->in_features, cfg->rank, nvfp4, act_codes, act_scales,
+                     act_global_scale, wgt_codes, wgt_scales, wgt_global_scale, lora_act, l2, bias,
+                     act, out_dtype == SVDQ_DT_BF16 ? 1 : 0, out};
+    if (nvfp4) svdq::launch_gemm_nvfp4(a, reinterpret_cast<hipStream_t>(stream));
+    else svdq::launch_gemm_int4(a, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_gemm_w4a4");
+}
+
+svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, const void* x,
+                           const void* qweight, const void* scales, const void* zeros,
+                           const void* bias, int32_t out_dtype, void* out, svdq_stream_t stream) {
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    if (K <= 0 || K % 64 != 0) return fail(SVDQ_ERR_INVALID_ARG, "K %d must be a positive multiple of 64", K);
+    if (N <= 0) return fail(SVDQ_ERR_INVALID_ARG, "N %d must be positive", N);
+    if (group_size != 64) return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "group_size %d: only 64 is supported", group_size);
+    if (out_dtype != SVDQ_DT_F32 && out_dtype != SVDQ_DT_BF16)
+        return fail(SVDQ_ERR_INVALID_ARG, "out_dtype %d is not a svdq_dtype value", out_dtype);
+    SVDQ_TRY(check_ptr(x, "x", 16));
+    SVDQ_TRY(check_ptr(qweight, "qweight", 16));
+    SVDQ_TRY(check_ptr(scales, "scales", 2));
+    SVDQ_TRY(check_ptr(zeros, "zeros", 2));
+    SVDQ_TRY(check_ptr(out, "out", out_dtype == SVDQ_DT_F32 ? 4 : 2));
+    if (bias != nullptr && !aligned(bias, 2)) return fail(SVDQ_ERR_INVALID_ARG, "bias is not 2-byte aligned");
+    SVDQ_TRY(check_current_device());
+    if (M == 0) return SVDQ_OK;
+    svdq::AwqArgs a{M, K, N, x, qweight, scales, zeros, bias, out_dtype == SVDQ_DT_BF16 ? 1 : 0, out};
+    svdq::launch_awq_gemv(a, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("awq_gemm_w4a16");
+}
+
+svdq_status svdq_check_device(int device) { return check_device_ordinal(device); }
+
+svdq_status svdq_check_arch(const char* arch_name) {
+    if (arch_name == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "arch_name is NULL");
+    if (!arch_is_gfx950(arch_name))
+        return fail(SVDQ_ERR_UNSUPPORTED_DEVICE, "architecture %s is not gfx950", arch_name);
+    return SVDQ_OK;
+}
+
+const char* svdq_status_string(svdq_status status) {
+    switch (status) {
+        case SVDQ_OK: return "SVDQ_OK";
+        case SVDQ_ERR_INVALID_ARG: return "SVDQ_ERR_INVALID_ARG: invalid argument";
+        case SVDQ_ERR_UNSUPPORTED_DEVICE: return "SVDQ_ERR_UNSUPPORTED_DEVICE: device is not gfx950";
+        case SVDQ_ERR_UNSUPPORTED_CONFIG: return "SVDQ_ERR_UNSUPPORTED_CONFIG: configuration not supported";
+        case SVDQ_ERR_LAUNCH: return "SVDQ_ERR_LAUNCH: kernel launch failed";
+    }
+    return "unknown svdq_status";
+}
+
+const char* svdq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t svdq_version(void) { return 100; }
+
+}  // extern "C"

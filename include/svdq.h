@@ -1,0 +1,169 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 / AWQ W4A16 linear library.
+ *
+ * The operation (pages, in their own words restated):
+ *   [margrop] "Hugging Face 把 Nunchaku 4-bit Diffusion 接到 Diffusers" (blog.margrop.com),
+ *             技术细节 1, "SVDQuant 的核心思路": activation outliers are migrated into the
+ *             weights; the hardest part of each weight is kept as a 16-bit low-rank branch;
+ *             the residual runs with 4-bit weights and activations; the low-rank
+ *             down-projection is fused into the quantization kernel and the up-projection
+ *             into the 4-bit compute kernel.
+ *   [margrop] 技术细节 3: kernel families svdq_w4a4 (precision int4 or nvfp4) and
+ *             awq_w4a16 (int4); loading on an unsupported GPU fails with a clear error and
+ *             never returns wrong results.
+ *   [ainews]  "Diffusers Natively Integrates Nunchaku Lite, Using W4A4 ...", paragraphs 2-3:
+ *             config.json records method, precision, group size, low-rank rank and target
+ *             modules; attention/MLP projections use SVDQ W4A4, modulation layers AWQ W4A16.
+ *
+ * A linear layer y = x W^T + b runs as two calls:
+ *   svdq_quantize_act : x (bf16) -> 4-bit codes + scales of x * diag(smooth_inv), and
+ *                       lora_act = x . L1^T (bf16), in one pass over x;
+ *   svdq_gemm_w4a4    : y = dequant(codes_x) . dequant(codes_w)^T + lora_act . L2^T + b
+ *                       (optionally GELU-tanh), fp32 or bf16 output.
+ * and the modulation layers as one call, awq_gemm_w4a16.
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller allocates and owns every buffer (device memory unless stated).
+ *     The library allocates nothing, keeps no pointer after a call returns, and enqueues
+ *     its work asynchronously on `stream` (0 = the null stream); buffers must stay alive
+ *     until that work completes.
+ *   - Layouts are row-major and dense.  "bf16" is the 16-bit brain float, passed as raw
+ *     16-bit words.
+ *   - Errors: every function validates its arguments before launching anything and returns
+ *     a status; on a non-OK status nothing was enqueued.  A thread-local message with the
+ *     detail is available from svdq_last_error().  Faults inside a kernel surface, as for
+ *     any HIP work, at the caller's next synchronisation.
+ *   - Device: the current HIP device must be an MI355X-class gfx950 GPU; any other device
+ *     yields SVDQ_ERR_UNSUPPORTED_DEVICE (checked once per device and cached).
+ *   - M = 0 is valid and enqueues nothing.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* svdq_stream_t;   /* same type as hipStream_t */
+
+typedef enum {
+    SVDQ_OK = 0,
+    SVDQ_ERR_INVALID_ARG = 1,        /* bad shape, null or misaligned pointer, bad enum */
+    SVDQ_ERR_UNSUPPORTED_DEVICE = 2, /* current device is not gfx950 */
+    SVDQ_ERR_UNSUPPORTED_CONFIG = 3, /* well-formed but not implemented (e.g. rank > 128) */
+    SVDQ_ERR_LAUNCH = 4              /* the HIP runtime refused a launch */
+} svdq_status;
+
+typedef enum { SVDQ_PREC_INT4 = 0, SVDQ_PREC_NVFP4 = 1 } svdq_precision;
+typedef enum { SVDQ_DT_F32 = 0, SVDQ_DT_BF16 = 1 } svdq_dtype;
+typedef enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 } svdq_act;
+
+/* The quantization fields a checkpoint's config.json records for one layer
+ * ([ainews] paragraph 2: method, precision, group size, low-rank rank). */
+typedef struct {
+    int32_t in_features;   /* K: a positive multiple of 64 */
+    int32_t out_features;  /* N: >= 1 */
+    int32_t rank;          /* r: 0, or a multiple of 16 up to 128 */
+    int32_t group_size;    /* 64 for INT4, 16 for NVFP4 */
+    int32_t precision;     /* svdq_precision */
+} svdq_layer_cfg;
+
+/*
+ * svdq_quantize_act -- the activation kernel of an SVDQ W4A4 layer.
+ * ([margrop] 技术细节 1 steps 1, 3 and 4.)
+ *
+ *   x          [M, K] bf16, device.                      Read only.
+ *   smooth_inv [K] fp32, device: 1/lambda per input channel (outliers migrated to W).
+ *   l1         [r, K] bf16, device, the low-rank down factor with 1/lambda absorbed;
+ *              may be NULL when r == 0.
+ *   act_global_scale  NVFP4 only: the activation's per-tensor fp32 scale S_a (> 0, finite);
+ *              ignored for INT4.
+ *   act_codes  [M, K/2] bytes, device, written: two 4-bit codes per byte, the even
+ *              channel in the low nibble.  INT4: two's-complement codes
+ *              q = clamp(rne(x_hat / s), -8, 7) with x_hat = fp32(x) * smooth_inv (one
+ *              fp32 multiply), s = absmax_group(|x_hat|) / 7 (fp32 division), groups of 64
+ *              channels, q = 0 where s = 0 (codes are always in [-7, 7]).
+ *              NVFP4: E2M1 codes (sign in bit 3) of x_hat / (sb * S_a) rounded to nearest,
+ *              ties to even, saturating at 6, per block of 16 channels.
+ *   act_scales INT4: [M, K/64] fp32 s.  NVFP4: [M, K/16] E4M3 bytes
+ *              sb = E4M3(min(absmax / (6 * S_a), 448)) (nearest, ties to even); codes are 0
+ *              where sb = 0.  Device, written.
+ *   lora_act   [M, r] bf16, device, written: bf16(sum_k x[m,k] * l1[j,k]) accumulated in
+ *              fp32 (may differ from a correctly rounded fp64 sum by one bf16 ulp).
+ *              May be NULL when r == 0.
+ * Pointers must be 16-byte aligned.  Quantized codes and scales are bit-exact functions
+ * of the inputs (no dependence on launch shape or run).
+ */
+svdq_status svdq_quantize_act(const svdq_layer_cfg* cfg, int64_t M, const void* x,
+                              const float* smooth_inv, const void* l1,
+                              float act_global_scale, void* act_codes, void* act_scales,
+                              void* lora_act, svdq_stream_t stream);
+
+/*
+ * svdq_gemm_w4a4 -- the 4-bit x 4-bit GEMM of an SVDQ W4A4 layer with the low-rank
+ * up-projection and bias in its epilogue ([margrop] 技术细节 1 step 4).
+ *
+ *   act_codes, act_scales, act_global_scale : as written by svdq_quantize_act.
+ *   wgt_codes  [N, K/2] bytes: the residual weight codes, same format as act_codes
+ *              (INT4 codes must lie in [-8, 7]; NVFP4 codes any E2M1 value).
+ *   wgt_scales INT4: [N, K/64] fp32.  NVFP4: [N, K/16] E4M3 bytes.
+ *   wgt_global_scale  NVFP4 only: S_w (> 0, finite); ignored for INT4.
+ *   lora_act   [M, r] bf16 (from svdq_quantize_act); l2 [N, r] bf16, the up factor.
+ *              Both may be NULL when r == 0.
+ *   bias       [N] bf16 or NULL.
+ *   act        svdq_act: SVDQ_ACT_GELU_TANH applies 0.5 y (1 + tanh(sqrt(2/pi)(y + 0.044715 y^3)))
+ *              after the bias (the fused GELU of a DiT MLP's first linear).
+ *   out_dtype  svdq_dtype of `out`.
+ *   out        [M, N] device, written:
+ *              INT4:  y = sum_g sa[m,g] sw[n,g] sum_{k in g} qa[m,k] qw[n,k]
+ *              NVFP4: y = S_a S_w sum_k e_a[m,k] sb_a[m,k/16] e_w[n,k] sb_w[n,k/16]
+ *              plus sum_j lora_act[m,j] l2[n,j] + bias[n], accumulated in fp32.
+ */
+svdq_status svdq_gemm_w4a4(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
+                           const void* act_scales, float act_global_scale,
+                           const void* wgt_codes, const void* wgt_scales,
+                           float wgt_global_scale, const void* lora_act, const void* l2,
+                           const void* bias, int32_t act, int32_t out_dtype, void* out,
+                           svdq_stream_t stream);
+
+/*
+ * awq_gemm_w4a16 -- AWQ W4A16 GEMV / skinny GEMM for modulation layers ([ainews]
+ * paragraph 3; [margrop] 技术细节 3, awq_w4a16 int4).
+ *
+ *   x        [M, K] bf16 (the per-channel AWQ scale already folded into x).
+ *   qweight  [N, K/2] bytes: unsigned 4-bit q, even channel in the low nibble.
+ *   scales   [N, K/group_size] bf16;  zeros [N, K/group_size] bf16 (integer values).
+ *   bias     [N] bf16 or NULL.
+ *   out      [M, N] fp32 or bf16: y = sum_k x[m,k] (q[n,k] - z[n,g]) s[n,g] + bias[n],
+ *            accumulated in fp32.
+ * group_size must be 64; K a multiple of 64; M <= 64.
+ */
+svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, const void* x,
+                           const void* qweight, const void* scales, const void* zeros,
+                           const void* bias, int32_t out_dtype, void* out,
+                           svdq_stream_t stream);
+
+/* SVDQ_OK when HIP device `device` is a gfx950 GPU, else SVDQ_ERR_UNSUPPORTED_DEVICE
+ * (or SVDQ_ERR_INVALID_ARG for a bad ordinal).  Results are cached per device. */
+svdq_status svdq_check_device(int device);
+
+/* Host-only check of an architecture name as HIP reports it (e.g. "gfx950:sramecc+:xnack-"):
+ * SVDQ_OK for gfx950, SVDQ_ERR_UNSUPPORTED_DEVICE otherwise, SVDQ_ERR_INVALID_ARG for NULL. */
+svdq_status svdq_check_arch(const char* arch_name);
+
+/* Static description of a status code. */
+const char* svdq_status_string(svdq_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* svdq_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t svdq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

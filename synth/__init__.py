@@ -28,11 +28,15 @@ def f32_to_bf16_bits(a):
     """Round float32 values to bf16 (nearest, ties to even) -> uint16 bit patterns.
     (A dtype conversion of the synthetic inputs, not part of the method.)"""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
+    u = a.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    lsb += np.uint32(0x7FFF)
+    lsb += u                      # wraps only for NaN bit patterns, replaced below
+    lsb >>= np.uint32(16)
+    out = lsb.astype(np.uint16)
     nan = np.isnan(a)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = u.astype(np.uint16)
-    out[nan] = 0x7FC0
+    if nan.any():
+        out[nan] = 0x7FC0
     return out
 
 

@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/svdq.h declares, and rejects bad arguments before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_diffusion_amd as bd
+from bit_diffusion_amd import _abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "svdq.h")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_and_library_exports_agree():
+    names = _declared_functions()
+    assert set(names) == set(_abi.EXPORTS), names
+    L = bd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert bd.svdq_version() == 100
+
+
+def test_arch_check_strings():
+    assert bd.svdq_check_arch("gfx950") == bd.SVDQ_OK
+    assert bd.svdq_check_arch("gfx950:sramecc+:xnack-") == bd.SVDQ_OK
+    for bad in ("gfx942", "gfx9500", "gfx90a:xnack+", "sm_90", ""):
+        assert bd.svdq_check_arch(bad) == bd.SVDQ_ERR_UNSUPPORTED_DEVICE, bad
+        assert "not gfx950" in bd.svdq_last_error()
+    assert bd.lib().svdq_check_arch(None) == bd.SVDQ_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(5):
+        assert bd.svdq_status_string(s).startswith("SVDQ_")
+    assert "unknown" in bd.svdq_status_string(99)
+
+
+# A fake, 256-byte aligned address: validation must fail before it is ever dereferenced.
+FAKE = 1 << 20
+
+
+def _quant(cfg, M=16, **kw):
+    args = dict(x=FAKE, smooth_inv=FAKE, l1=FAKE, S=1.0, codes=FAKE, scales=FAKE, lora=FAKE)
+    args.update(kw)
+    return bd.lib().svdq_quantize_act(
+        ctypes.byref(cfg) if cfg is not None else None, M, args["x"], args["smooth_inv"],
+        args["l1"], args["S"], args["codes"], args["scales"], args["lora"], None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("in_features", 100, bd.SVDQ_ERR_INVALID_ARG),
+    ("in_features", 0, bd.SVDQ_ERR_INVALID_ARG),
+    ("out_features", 0, bd.SVDQ_ERR_INVALID_ARG),
+    ("rank", 8, bd.SVDQ_ERR_INVALID_ARG),
+    ("rank", 144, bd.SVDQ_ERR_UNSUPPORTED_CONFIG),
+    ("group_size", 128, bd.SVDQ_ERR_INVALID_ARG),
+    ("precision", 7, bd.SVDQ_ERR_INVALID_ARG),
+])
+def test_quantize_rejects_bad_cfg(field, value, status):
+    cfg = bd.LayerCfg.make(512, 512, 16)
+    setattr(cfg, field, value)
+    assert _quant(cfg) == status
+    assert bd.svdq_last_error() != ""
+
+
+def test_quantize_rejects_null_misaligned_and_negative():
+    cfg = bd.LayerCfg.make(512, 512, 16)
+    assert _quant(None) == bd.SVDQ_ERR_INVALID_ARG
+    assert _quant(cfg, x=None) == bd.SVDQ_ERR_INVALID_ARG and "x is NULL" in bd.svdq_last_error()
+    assert _quant(cfg, x=FAKE + 8) == bd.SVDQ_ERR_INVALID_ARG
+    assert "aligned" in bd.svdq_last_error()
+    assert _quant(cfg, l1=None) == bd.SVDQ_ERR_INVALID_ARG
+    assert _quant(cfg, M=-1) == bd.SVDQ_ERR_INVALID_ARG
+    nv = bd.LayerCfg.make(512, 512, 16, "nvfp4")
+    for S in (0.0, -1.0, float("inf"), float("nan")):
+        assert _quant(nv, S=S) == bd.SVDQ_ERR_INVALID_ARG
+
+
+def test_gemm_rejects_bad_args():
+    L = bd.lib()
+    cfg = bd.LayerCfg.make(512, 512, 16)
+
+    def call(cfg=cfg, act=0, dt=0, out=FAKE, lora=FAKE, M=16, Sa=1.0, Sw=1.0):
+        return L.svdq_gemm_w4a4(ctypes.byref(cfg), M, FAKE, FAKE, Sa, FAKE, FAKE, Sw, lora, FAKE,
+                                None, act, dt, out, None)
+
+    assert call(act=2) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(dt=3) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(out=None) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(lora=None) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(M=-5) == bd.SVDQ_ERR_INVALID_ARG
+    nv = bd.LayerCfg.make(512, 512, 16, "nvfp4")
+    assert call(cfg=nv, Sw=0.0) == bd.SVDQ_ERR_INVALID_ARG
+
+
+def test_awq_rejects_bad_args():
+    L = bd.lib()
+
+    def call(M=2, K=3072, N=64, gs=64, dt=0, x=FAKE):
+        return L.awq_gemm_w4a16(M, K, N, gs, x, FAKE, FAKE, FAKE, None, dt, FAKE, None)
+
+    assert call(K=100) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(N=0) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(gs=128) == bd.SVDQ_ERR_UNSUPPORTED_CONFIG
+    assert call(dt=9) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(x=None) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(M=-1) == bd.SVDQ_ERR_INVALID_ARG
+
+
+def test_python_binding_raises_with_message():
+    cfg = bd.LayerCfg.make(100, 512, 16)
+    with pytest.raises(bd.SvdqError) as e:
+        bd.svdq_quantize_act(cfg, 4, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == bd.SVDQ_ERR_INVALID_ARG and "in_features" in e.value.message

@@ -1,0 +1,143 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times:
+  attention projection 4096x3072x3072 r32 (INT4), the DiT MLP pair 4608x3072->12288->3072
+  with GELU (INT4), the fused-QKV NVFP4 projection 4096x3072x9216 r32 and the AWQ GEMV
+  2x3072x18432.  Weights come from the oracle's offline construction (smoothing factors,
+  top-r factors, quantized residual).
+
+Per stage, the GPU kernel is fed the oracle's inputs (never the other way round): the
+activation kernel is compared in full (codes and scales bit-exact, lora_act within its
+bound); the GEMM, fed the oracle's activation-stage outputs, on sampled elements (random
+points, whole rows and whole columns) that the oracle computes one by one.  End to end,
+the GPU chain and the oracle chain each run from the same X and are compared.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.construct import bf16_from_f64_vec, build_workload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+gu = pytest.importorskip("gpu_util")
+
+
+def _get(cache, idx):
+    if idx not in cache:
+        cache[idx] = build_workload(synth.WORKLOADS[idx])
+    return cache[idx]
+
+
+def _samples(rng, M, N, n_pts=3000):
+    mi = rng.integers(0, M, n_pts)
+    ni = rng.integers(0, N, n_pts)
+    rows = np.array([0, M - 1, M // 2])
+    cols = np.array([0, N - 1])
+    mi = np.concatenate([mi, np.repeat(rows, N), np.tile(np.arange(M), len(cols))])
+    ni = np.concatenate([ni, np.tile(np.arange(N), len(rows)), np.repeat(cols, M)])
+    return mi, ni
+
+
+def _quant_exact(xb, L, precision="int4", S=1.0):
+    """GPU activation kernel vs oracle on the same input; returns both."""
+    codes, scales, lora = gu.quantize(xb, L["smooth_inv"], L["l1"], precision, float(S))
+    torch.cuda.synchronize()
+    if precision == "int4":
+        oc, os_, ol = oracle.quant_act_int4(xb, L["smooth_inv"], L["l1"])
+    else:
+        oc, os_, ol = oracle.quant_act_nvfp4(xb, L["smooth_inv"], S, L["l1"])
+    gc, gs, gl = gu.host(codes), gu.host(scales), gu.host(lora)
+    assert np.array_equal(gc, oc), f"codes differ in {np.count_nonzero(gc != oc)} bytes"
+    assert np.array_equal(gs.view(np.uint8), os_.view(np.uint8)), "scales differ"
+    gu.assert_lora_close(gl, ol, xb, L["l1"])
+    return (codes, scales, lora), (oc, os_, ol)
+
+
+def test_attn_projection_int4(workload_cache):
+    d, (L,) = _get(workload_cache, 1)
+    (gc, gs, gl), (oc, os_, ol) = _quant_exact(d.x_bf16, L)
+    rng = np.random.default_rng(1)
+    # GEMM stage on the oracle's activation-stage outputs
+    y = gu.host(gu.gemm(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], L["bias"]))
+    mi, ni = _samples(rng, *y.shape)
+    ref = oracle.gemm_w4a4_int4_at(mi, ni, oc, os_, L["wcodes"], L["wscales"], ol, L["l2"],
+                                   L["bias"])
+    e = gu.rel_fro(y[mi, ni], ref)
+    print(f"attn int4 gemm rel_fro={e:.3e}")
+    assert e <= 1e-3
+    yb = gu.host(gu.gemm(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], L["bias"],
+                         out_bf16=True))
+    gu.assert_bf16_close(yb[mi, ni], ref)
+    # end to end: GPU chain vs oracle chain from the same X
+    ye = gu.host(gu.gemm(gc, gs, L["wcodes"], L["wscales"], gl, L["l2"], L["bias"]))
+    e2e = gu.rel_fro(ye[mi, ni], ref)
+    print(f"attn int4 end-to-end rel_fro={e2e:.3e}")
+    assert e2e <= 1e-3
+
+
+def test_mlp_pair_int4(workload_cache):
+    d, (L1, L2) = _get(workload_cache, 2)
+    rng = np.random.default_rng(2)
+    # fc1: activation kernel in full, then GEMM with fused GELU and bf16 output
+    (gc1, gs1, gl1), (oc1, os1, ol1) = _quant_exact(d.x_bf16, L1)
+    h_or = gu.host(gu.gemm(oc1, os1, L1["wcodes"], L1["wscales"], ol1, L1["l2"], L1["bias"],
+                           act=1, out_bf16=True))
+    mi1, ni1 = _samples(rng, *h_or.shape, n_pts=2000)
+    ref1 = oracle.gemm_w4a4_int4_at(mi1, ni1, oc1, os1, L1["wcodes"], L1["wscales"], ol1,
+                                    L1["l2"], L1["bias"], act=1)
+    # bf16 rounding alone is ~1.5e-3 relative: compare at the same rounding point
+    gu.assert_bf16_close(h_or[mi1, ni1], ref1)
+    # the oracle's chain on a few token rows: fc1 -> GELU (fp64) -> bf16 -> fc2
+    rows = np.array([0, 1, 777, 2048, 4095, d.x_bf16.shape[0] - 1])
+    y1 = oracle.gemm_w4a4_int4(oc1[rows], os1[rows], L1["wcodes"], L1["wscales"], ol1[rows],
+                               L1["l2"], L1["bias"], act=1)
+    h_rows = bf16_from_f64_vec(y1)
+    # fc2's activation kernel on the oracle's intermediate rows: bit-exact
+    _, (qc, qs, ql) = _quant_exact(h_rows, L2)
+    y2 = oracle.gemm_w4a4_int4(qc, qs, L2["wcodes"], L2["wscales"], ql, L2["l2"], L2["bias"])
+    # GPU chain end to end: quant -> GEMM+GELU (bf16) -> quant -> GEMM
+    h = gu.gemm(gc1, gs1, L1["wcodes"], L1["wscales"], gl1, L1["l2"], L1["bias"], act=1,
+                out_bf16=True)
+    c2, s2, lo2 = gu.quantize(h, L2["smooth_inv"], L2["l1"])
+    y = gu.host(gu.gemm(c2, s2, L2["wcodes"], L2["wscales"], lo2, L2["l2"], L2["bias"]))
+    e2e = gu.rel_fro(y[rows], y2)
+    print(f"mlp end-to-end rel_fro={e2e:.3e}")
+    assert e2e <= 1e-3
+    # fc2 standalone on its heavy-tailed calibration input
+    _, (oc3, os3, ol3) = _quant_exact(d.extras["x2_bf16"], L2)
+    y3 = gu.host(gu.gemm(oc3, os3, L2["wcodes"], L2["wscales"], ol3, L2["l2"], L2["bias"]))
+    mi3, ni3 = _samples(rng, *y3.shape, n_pts=2000)
+    ref3 = oracle.gemm_w4a4_int4_at(mi3, ni3, oc3, os3, L2["wcodes"], L2["wscales"], ol3,
+                                    L2["l2"], L2["bias"])
+    e3 = gu.rel_fro(y3[mi3, ni3], ref3)
+    print(f"mlp fc2 gemm rel_fro={e3:.3e}")
+    assert e3 <= 1e-3
+
+
+def test_qkv_nvfp4(workload_cache):
+    d, (L,) = _get(workload_cache, 3)
+    (gc, gs, gl), (oc, os_, ol) = _quant_exact(d.x_bf16, L, "nvfp4", L["Sa"])
+    kw = dict(precision="nvfp4", Sa=float(L["Sa"]), Sw=float(L["Sw"]))
+    y = gu.host(gu.gemm(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], L["bias"], **kw))
+    rng = np.random.default_rng(3)
+    mi, ni = _samples(rng, *y.shape)
+    ref = oracle.gemm_w4a4_nvfp4_at(mi, ni, oc, os_, L["Sa"], L["wcodes"], L["wscales"],
+                                    L["Sw"], ol, L["l2"], L["bias"])
+    e = gu.rel_fro(y[mi, ni], ref)
+    print(f"qkv nvfp4 gemm rel_fro={e:.3e}")
+    assert e <= 1e-3
+    ye = gu.host(gu.gemm(gc, gs, L["wcodes"], L["wscales"], gl, L["l2"], L["bias"], **kw))
+    assert gu.rel_fro(ye[mi, ni], ref) <= 1e-3
+
+
+def test_awq_modulation_gemv(workload_cache):
+    d, (A,) = _get(workload_cache, 4)
+    y = gu.host(gu.awq(A["x_prime"], A["qweight"], A["scales"], A["zeros"], A["bias"]))
+    ref = oracle.awq_gemv(A["x_prime"], A["qweight"], A["scales"], A["zeros"], A["bias"])
+    e = gu.rel_fro(y, ref)
+    print(f"awq rel_fro={e:.3e}")
+    assert e <= 1e-3
+    yb = gu.host(gu.awq(A["x_prime"], A["qweight"], A["scales"], A["zeros"], A["bias"],
+                        out_bf16=True))
+    gu.assert_bf16_close(yb, ref)
