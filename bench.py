@@ -82,8 +82,10 @@ def make_inputs(copies):
         ws = torch.empty((N, K // 64), dtype=torch.float32, device=dev)
         bd.svdq_quantize_act(cfg_w, N, rt, ones, None, 1.0, wc, ws, None)
         del rt
+        packed = torch.empty(bd.svdq_prepacked_weight_bytes(cfg_w), dtype=torch.uint8, device=dev)
+        bd.svdq_prepack_weight(cfg_w, wc, ws, packed)
         s = dict(
-            x=x, wc=wc, ws=ws,
+            x=x, wc=wc, ws=ws, packed=packed,
             l1=t16(synth.random_bf16(rng, (R, K), 0.02)),
             l2=t16(synth.random_bf16(rng, (N, R), 0.02)),
             bias=t16(d.bias_bf16),
@@ -138,12 +140,15 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
+    def gemm(s):
+        bd.svdq_gemm_w4a4_prepacked(cfg, M, s["codes"], s["scales"], s["packed"], s["lora"],
+                                    s["l2"], s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16,
+                                    s["out"], sp)
+
     def step(s):
         bd.svdq_quantize_act(cfg, M, s["x"], si, s["l1"], 1.0, s["codes"], s["scales"],
                              s["lora"], sp)
-        bd.svdq_gemm_w4a4(cfg, M, s["codes"], s["scales"], 1.0, s["wc"], s["ws"], 1.0,
-                          s["lora"], s["l2"], s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16,
-                          s["out"], sp)
+        gemm(s)
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
@@ -166,9 +171,7 @@ def main():
         bd.svdq_quantize_act(cfg, M, s["x"], si, s["l1"], 1.0, s["codes"], s["scales"],
                              s["lora"], sp)
         evs[3 * i + 1].record(stream)
-        bd.svdq_gemm_w4a4(cfg, M, s["codes"], s["scales"], 1.0, s["wc"], s["ws"], 1.0,
-                          s["lora"], s["l2"], s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16,
-                          s["out"], sp)
+        gemm(s)
         evs[3 * i + 2].record(stream)
     torch.cuda.synchronize()
     t_q = np.array([evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(args.steps)])
@@ -199,7 +202,7 @@ def main():
                    round(100 * value / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": None, "kernel": "svdq_gemm_w4a4 (int4)",
+                     "traffic": None, "kernel": "svdq_gemm_w4a4_prepacked (int4, FP6 MFMA)",
                      "ms_per_launch": round(float(t_g.mean()), 5)},
         "kernels": {
             "quantize_act_ms": round(float(t_q.mean()), 5),

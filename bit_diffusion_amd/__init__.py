@@ -17,6 +17,7 @@ from ._abi import (SVDQ_OK, SVDQ_ERR_INVALID_ARG, SVDQ_ERR_UNSUPPORTED_DEVICE,  
 
 __all__ = [
     "svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_device",
+    "svdq_prepacked_weight_bytes", "svdq_prepack_weight", "svdq_gemm_w4a4_prepacked",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -69,6 +70,25 @@ def awq_gemm_w4a16(M, K, N, group_size, x, qweight, scales, zeros, bias, out_dty
     return _check(L.awq_gemm_w4a16(int(M), int(K), int(N), int(group_size), _ptr(x),
                                    _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(bias),
                                    int(out_dtype), _ptr(out), _stream(stream)))
+
+
+def svdq_prepacked_weight_bytes(cfg):
+    n = ctypes.c_int64(0)
+    _check(lib().svdq_prepacked_weight_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def svdq_prepack_weight(cfg, wgt_codes, wgt_scales, prepacked, stream=None):
+    return _check(lib().svdq_prepack_weight(ctypes.byref(cfg), _ptr(wgt_codes), _ptr(wgt_scales),
+                                            _ptr(prepacked), _stream(stream)))
+
+
+def svdq_gemm_w4a4_prepacked(cfg, M, act_codes, act_scales, prepacked, lora_act, l2, bias, act,
+                             out_dtype, out, stream=None):
+    return _check(lib().svdq_gemm_w4a4_prepacked(
+        ctypes.byref(cfg), int(M), _ptr(act_codes), _ptr(act_scales), _ptr(prepacked),
+        _ptr(lora_act), _ptr(l2), _ptr(bias), int(act), int(out_dtype), _ptr(out),
+        _stream(stream)))
 
 
 def svdq_check_device(device=0):

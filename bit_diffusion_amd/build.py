@@ -25,12 +25,15 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["api.hip", "quant.hip", "gemm_int4.hip", "gemm_nvfp4.hip", "awq.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm_int4.hip", "gemm_int4_fp6.hip", "gemm_nvfp4.hip",
+           "awq.hip"]
+# per-source extra flags: MFMA results in VGPRs (the fp32 rescale reads them with VALU ops)
+EXTRA = {"gemm_int4_fp6.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

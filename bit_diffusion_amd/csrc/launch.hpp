@@ -49,9 +49,32 @@ struct AwqArgs {
     void* out;
 };
 
+struct PrepackedGemmArgs {
+    int64_t M;
+    int N, K, r;
+    int ntiles_padded;
+    const void* acodes;
+    const void* ascales;
+    const void* prepacked;
+    const void* lora;
+    const void* l2;
+    const void* bias;
+    int act;
+    int out_bf16;
+    void* out;
+};
+
+size_t quantize_act_lds_bytes(int K, int r);
 void launch_quantize_act(const QuantArgs& a, hipStream_t st);
 void launch_gemm_int4(const GemmArgs& a, hipStream_t st);
 void launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);
 void launch_awq_gemv(const AwqArgs& a, hipStream_t st);
+
+int64_t prepacked_int4_bytes(int N, int K);
+int prepacked_ntiles_padded(int N);
+void launch_prepack_int4(int N, int K, const void* wcodes, const void* wscales, void* out,
+                         hipStream_t st);
+bool gemm_int4_fp6_init();
+void launch_gemm_int4_fp6(const PrepackedGemmArgs& a, hipStream_t st);
 
 }  // namespace svdq

@@ -23,7 +23,6 @@ namespace svdq {
 namespace {
 
 constexpr int kRows = 16;
-constexpr int kWaves = 8;
 constexpr float kMinNormal = 1.17549435e-38f;
 
 // rne(xh / s) clamped to [-8, 7], with the fp32 quotient correctly rounded as the code's
@@ -67,70 +66,121 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v) {
     return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
-struct Tile16 {
-    uint4 xv0, xv1;      // 16 bf16 of one row
-    float xh[16];        // smoothed fp32
+// ---------------------------------------------------------------------------------------
+// Work mapping: a block of 16 waves owns 16 token rows; wave w walks groups w, w+16, ...
+// Lane l holds row (l % 16) and the 16 consecutive channels 16 * (l / 16) .. +15 of the
+// current 64-channel group: the A-operand layout of two v_mfma_f32_16x16x32_bf16 (one per
+// 32-channel half) for the low-rank down-projection.  The next group's activations and L1
+// slice are loaded while the current group is processed; smooth_inv sits in LDS.
+
+constexpr int kQWaves = 16;
+constexpr size_t kQuantMaxLds = 160 * 1024;
+constexpr int kQThreads = kQWaves * 64;
+
+// Up to rank 32 the next group's L1 slice is prefetched with its activations; beyond that
+// the registers would spill, and L1 is loaded when it is used.
+template <int RB>
+constexpr bool kPrefetchL1 = RB <= 2;
+
+template <int RB>
+struct Stage16 {
+    uint4 xv0, xv1;                                    // 16 bf16 of one row
+    uint4 l1v[kPrefetchL1<RB> && RB > 0 ? 2 * RB : 1]; // L1 rows (16 b + row), this group
 };
 
-__device__ __forceinline__ void load_tile(Tile16& t, const uint16_t* xr, const float* si, int k0) {
-    t.xv0 = *reinterpret_cast<const uint4*>(xr + k0);
-    t.xv1 = *reinterpret_cast<const uint4*>(xr + k0 + 8);
-    const float4* sp = reinterpret_cast<const float4*>(si + k0);
-    float4 s[4] = {sp[0], sp[1], sp[2], sp[3]};
-    uint32_t w[8] = {t.xv0.x, t.xv0.y, t.xv0.z, t.xv0.w, t.xv1.x, t.xv1.y, t.xv1.z, t.xv1.w};
+template <int RB>
+__device__ __forceinline__ void load_stage(Stage16<RB>& st, const uint16_t* xr, const uint16_t* l1,
+                                           int K, int rl, int k0) {
+    st.xv0 = *reinterpret_cast<const uint4*>(xr + k0);
+    st.xv1 = *reinterpret_cast<const uint4*>(xr + k0 + 8);
+    if constexpr (kPrefetchL1<RB>)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-        float sv = (&s[i >> 2].x)[i & 3];
-        t.xh[i] = bf16_to_f32(h) * sv;
+    for (int b = 0; b < RB; ++b) {
+        const uint16_t* lr = l1 + (int64_t)(b * 16 + rl) * K + k0;
+        st.l1v[2 * b] = *reinterpret_cast<const uint4*>(lr);
+        st.l1v[2 * b + 1] = *reinterpret_cast<const uint4*>(lr + 8);
     }
 }
 
-// Accumulate the 16x(16*RB) block of X . L1^T for this 64-channel group.
+// x_hat = fp32(x) * smooth_inv for the lane's 16 channels (smooth_inv from LDS).
 template <int RB>
-__device__ __forceinline__ void lowrank_step(f32x4 (&acc)[RB > 0 ? RB : 1], const Tile16& t,
+__device__ __forceinline__ void smooth16(float (&xh)[16], const Stage16<RB>& st, const float* si) {
+    const float4* sp = reinterpret_cast<const float4*>(si);
+    const float4 s4[4] = {sp[0], sp[1], sp[2], sp[3]};
+    const uint32_t w[8] = {st.xv0.x, st.xv0.y, st.xv0.z, st.xv0.w,
+                           st.xv1.x, st.xv1.y, st.xv1.z, st.xv1.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        xh[i] = bf16_to_f32(h) * (&s4[i >> 2].x)[i & 3];
+    }
+}
+
+template <int RB>
+__device__ __forceinline__ void lowrank_mfma(f32x4 (&acc)[RB > 0 ? RB : 1], const Stage16<RB>& st,
                                              const uint16_t* l1, int K, int rl, int k0) {
     if constexpr (RB > 0) {
-        bf16x8 a0 = as_bf16x8(t.xv0), a1 = as_bf16x8(t.xv1);
+        const bf16x8 a0 = as_bf16x8(st.xv0), a1 = as_bf16x8(st.xv1);
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-            const uint16_t* lr = l1 + (int64_t)(b * 16 + rl) * K + k0;
-            uint4 b0 = *reinterpret_cast<const uint4*>(lr);
-            uint4 b1 = *reinterpret_cast<const uint4*>(lr + 8);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(b0), acc[b], 0, 0, 0);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(b1), acc[b], 0, 0, 0);
+            uint4 v0, v1;
+            if constexpr (kPrefetchL1<RB>) {
+                v0 = st.l1v[2 * b];
+                v1 = st.l1v[2 * b + 1];
+            } else {
+                const uint16_t* lr = l1 + (int64_t)(b * 16 + rl) * K + k0;
+                v0 = *reinterpret_cast<const uint4*>(lr);
+                v1 = *reinterpret_cast<const uint4*>(lr + 8);
+            }
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(v0), acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(v1), acc[b], 0, 0, 0);
         }
     }
 }
 
-// Sum the per-wave partial products over the waves (fixed order) and store bf16 lora_act.
+// Sum the 16 waves' partial low-rank products in a fixed tree order and store bf16 lora_act.
+// red holds 8 waves x RB x 256 floats.
 template <int RB>
 __device__ __forceinline__ void lowrank_finish(f32x4 (&acc)[RB > 0 ? RB : 1], float* red,
                                                int64_t m0, int64_t M, uint16_t* lora) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if constexpr (RB > 0) {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int b = 0; b < RB; ++b)
+        for (int half = kQWaves / 2; half >= 1; half >>= 1) {
+            if (wave >= half && wave < 2 * half) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                red[((wave * RB + b) * 16 + (4 * (lane >> 4) + i)) * 16 + (lane & 15)] = acc[b][i];
-        __syncthreads();
-        for (int t = threadIdx.x; t < 256 * RB; t += blockDim.x) {
-            int b = t >> 8, rr = (t >> 4) & 15, cc = t & 15;
-            float s = 0.0f;
-            for (int w = 0; w < kWaves; ++w) s += red[((w * RB + b) * 16 + rr) * 16 + cc];
-            int64_t m = m0 + rr;
-            if (m < M) lora[m * (RB * 16) + b * 16 + cc] = (uint16_t)f32_to_bf16(s);
+                for (int b = 0; b < RB; ++b)
+                    *reinterpret_cast<f32x4*>(&red[(((wave - half) * RB + b) * 64 + lane) * 4]) = acc[b];
+            }
+            __syncthreads();
+            if (wave < half) {
+#pragma unroll
+                for (int b = 0; b < RB; ++b)
+                    acc[b] += *reinterpret_cast<const f32x4*>(&red[((wave * RB + b) * 64 + lane) * 4]);
+            }
+            __syncthreads();
+        }
+        if (wave == 0) {
+            // 16x16 output layout: lane holds rows 4 * (lane / 16) + i, column lane % 16
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t m = m0 + 4 * (lane >> 4) + i;
+                    if (m < M) lora[m * (RB * 16) + b * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(acc[b][i]);
+                }
         }
     }
 }
 
-template <int RB>
-__global__ __launch_bounds__(kWaves * 64) void quant_act_int4_kernel(
+template <int RB, bool kNvfp4>
+__global__ __launch_bounds__(kQThreads) void quant_act_kernel(
     int64_t M, int K, const uint16_t* __restrict__ x, const float* __restrict__ smooth_inv,
-    const uint16_t* __restrict__ l1, uint8_t* __restrict__ codes, float* __restrict__ scales,
+    const uint16_t* __restrict__ l1, float S, uint8_t* __restrict__ codes, void* __restrict__ scales,
     uint16_t* __restrict__ lora) {
-    __shared__ float red[RB > 0 ? kWaves * 256 * RB : 1];
+    extern __shared__ __align__(16) float qsm[];
+    float* si_lds = qsm;                     // K floats
+    float* red = qsm + K;                    // 8 * RB * 256 floats
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t m0 = (int64_t)blockIdx.x * kRows;
     const int rl = lane & 15, kc = (lane >> 4) * 16;
@@ -138,129 +188,104 @@ __global__ __launch_bounds__(kWaves * 64) void quant_act_int4_kernel(
     const bool valid = row < M;
     const uint16_t* xr = x + (valid ? row : M - 1) * (int64_t)K;
     const int G = K >> 6;
+    const int ng = G > wave ? (G - wave + kQWaves - 1) / kQWaves : 0;   // this wave's groups
     f32x4 acc[RB > 0 ? RB : 1];
 #pragma unroll
     for (int b = 0; b < (RB > 0 ? RB : 1); ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int g = wave; g < G; g += kWaves) {
-        const int k0 = g * 64 + kc;
-        Tile16 t;
-        load_tile(t, xr, smooth_inv, k0);
-        float a = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(t.xh[i]));
-        a = wave_max_xor(a, 16);
-        a = wave_max_xor(a, 32);
-        const float s = a / 7.0f;
-        uint32_t p0 = 0u, p1 = 0u;
-        if (s != 0.0f) {
-            const float rcp = 1.0f / s;
-            const bool exact_only = s < kMinNormal;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint32_t nib = (uint32_t)int4_code(t.xh[i], s, rcp, exact_only) & 15u;
-                if (i < 8) p0 |= nib << (4 * i);
-                else p1 |= nib << (4 * (i - 8));
-            }
-        }
-        if (valid) {
-            *reinterpret_cast<uint2*>(codes + row * (K / 2) + k0 / 2) = make_uint2(p0, p1);
-            if (kc == 0) scales[row * G + g] = s;
-        }
-        lowrank_step<RB>(acc, t, l1, K, rl, k0);
-    }
-    lowrank_finish<RB>(acc, red, m0, M, lora);
-}
-
-template <int RB>
-__global__ __launch_bounds__(kWaves * 64) void quant_act_nvfp4_kernel(
-    int64_t M, int K, const uint16_t* __restrict__ x, const float* __restrict__ smooth_inv,
-    const uint16_t* __restrict__ l1, float S, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, uint16_t* __restrict__ lora) {
-    __shared__ float red[RB > 0 ? kWaves * 256 * RB : 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t m0 = (int64_t)blockIdx.x * kRows;
-    const int rl = lane & 15, kc = (lane >> 4) * 16;
-    const int64_t row = m0 + rl;
-    const bool valid = row < M;
-    const uint16_t* xr = x + (valid ? row : M - 1) * (int64_t)K;
-    const int G = K >> 6;
+    Stage16<RB> cur, nxt;
+    if (ng > 0) load_stage<RB>(cur, xr, l1, K, rl, wave * 64 + kc);
+    for (int i = threadIdx.x * 4; i < K; i += kQThreads * 4)
+        *reinterpret_cast<float4*>(si_lds + i) = *reinterpret_cast<const float4*>(smooth_inv + i);
+    __syncthreads();
     const float den = 6.0f * S;
-    f32x4 acc[RB > 0 ? RB : 1];
-#pragma unroll
-    for (int b = 0; b < (RB > 0 ? RB : 1); ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int g = wave; g < G; g += kWaves) {
-        const int k0 = g * 64 + kc;   // this lane's 16 channels are one NVFP4 block
-        Tile16 t;
-        load_tile(t, xr, smooth_inv, k0);
+    for (int it = 0; it < ng; ++it) {
+        const int g = wave + it * kQWaves;
+        const int k0 = g * 64 + kc;
+        if (it + 1 < ng) load_stage<RB>(nxt, xr, l1, K, rl, k0 + kQWaves * 64);
+        float xh[16];
+        smooth16<RB>(xh, cur, si_lds + k0);
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(t.xh[i]));
-        const uint32_t sb = e4m3_encode(a / den);
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xh[i]));
         uint32_t p0 = 0u, p1 = 0u;
-        if (sb != 0u) {
-            const float d = e4m3_decode(sb) * S;
+        if constexpr (!kNvfp4) {
+            // INT4: the 64-channel group spans the four lanes of this row
+            a = wave_max_xor(a, 16);
+            a = wave_max_xor(a, 32);
+            const float s = a / 7.0f;
+            if (s != 0.0f) {
+                const float rcp = 1.0f / s;
+                const bool exact_only = s < kMinNormal;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint32_t c = e2m1_encode(t.xh[i] / d);
-                if (i < 8) p0 |= c << (4 * i);
-                else p1 |= c << (4 * (i - 8));
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t nib = (uint32_t)int4_code(xh[i], s, rcp, exact_only) & 15u;
+                    if (i < 8) p0 |= nib << (4 * i);
+                    else p1 |= nib << (4 * (i - 8));
+                }
             }
+            if (valid && kc == 0) reinterpret_cast<float*>(scales)[row * G + g] = s;
+        } else {
+            // NVFP4: this lane's 16 channels are one block
+            const uint32_t sb = e4m3_encode(a / den);
+            if (sb != 0u) {
+                const float d = e4m3_decode(sb) * S;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t c = e2m1_encode(xh[i] / d);
+                    if (i < 8) p0 |= c << (4 * i);
+                    else p1 |= c << (4 * (i - 8));
+                }
+            }
+            if (valid) reinterpret_cast<uint8_t*>(scales)[row * (K / 16) + k0 / 16] = (uint8_t)sb;
         }
-        if (valid) {
-            *reinterpret_cast<uint2*>(codes + row * (K / 2) + k0 / 2) = make_uint2(p0, p1);
-            scales[row * (K / 16) + k0 / 16] = (uint8_t)sb;
-        }
-        lowrank_step<RB>(acc, t, l1, K, rl, k0);
+        if (valid) *reinterpret_cast<uint2*>(codes + row * (K / 2) + k0 / 2) = make_uint2(p0, p1);
+        lowrank_mfma<RB>(acc, cur, l1, K, rl, k0);
+        if (it + 1 < ng) cur = nxt;
     }
     lowrank_finish<RB>(acc, red, m0, M, lora);
 }
 
 template <int RB>
-void launch_int4(const QuantArgs& a, hipStream_t st) {
-    dim3 grid((unsigned)((a.M + kRows - 1) / kRows)), block(kWaves * 64);
-    hipLaunchKernelGGL(quant_act_int4_kernel<RB>, grid, block, 0, st, a.M, a.K,
-                       (const uint16_t*)a.x, a.smooth_inv, (const uint16_t*)a.l1,
-                       (uint8_t*)a.codes, (float*)a.scales, (uint16_t*)a.lora);
-}
-
-template <int RB>
-void launch_nvfp4(const QuantArgs& a, hipStream_t st) {
-    dim3 grid((unsigned)((a.M + kRows - 1) / kRows)), block(kWaves * 64);
-    hipLaunchKernelGGL(quant_act_nvfp4_kernel<RB>, grid, block, 0, st, a.M, a.K,
-                       (const uint16_t*)a.x, a.smooth_inv, (const uint16_t*)a.l1, a.S,
-                       (uint8_t*)a.codes, (uint8_t*)a.scales, (uint16_t*)a.lora);
+void launch_rb(const QuantArgs& a, hipStream_t st) {
+    const size_t lds = ((size_t)a.K + 8 * (size_t)RB * 256) * sizeof(float);
+    dim3 grid((unsigned)((a.M + kRows - 1) / kRows)), block(kQThreads);
+    static bool attr_set[2] = {false, false};
+    if (!attr_set[a.nvfp4]) {
+        (void)hipFuncSetAttribute(a.nvfp4 ? (const void*)quant_act_kernel<RB, true>
+                                    : (const void*)quant_act_kernel<RB, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kQuantMaxLds);
+        attr_set[a.nvfp4] = true;
+    }
+    if (a.nvfp4) {
+        auto k = quant_act_kernel<RB, true>;
+        hipLaunchKernelGGL(k, grid, block, lds, st, a.M, a.K, (const uint16_t*)a.x, a.smooth_inv,
+                           (const uint16_t*)a.l1, a.S, (uint8_t*)a.codes, a.scales, (uint16_t*)a.lora);
+    } else {
+        auto k = quant_act_kernel<RB, false>;
+        hipLaunchKernelGGL(k, grid, block, lds, st, a.M, a.K, (const uint16_t*)a.x, a.smooth_inv,
+                           (const uint16_t*)a.l1, a.S, (uint8_t*)a.codes, a.scales, (uint16_t*)a.lora);
+    }
 }
 
 }  // namespace
 
+size_t quantize_act_lds_bytes(int K, int r) {
+    return ((size_t)K + 8 * (size_t)(r / 16) * 256) * sizeof(float);
+}
+
 void launch_quantize_act(const QuantArgs& a, hipStream_t st) {
-    const int rb = a.r / 16;
-    if (a.nvfp4) {
-        switch (rb) {
-            case 0: launch_nvfp4<0>(a, st); break;
-            case 1: launch_nvfp4<1>(a, st); break;
-            case 2: launch_nvfp4<2>(a, st); break;
-            case 3: launch_nvfp4<3>(a, st); break;
-            case 4: launch_nvfp4<4>(a, st); break;
-            case 5: launch_nvfp4<5>(a, st); break;
-            case 6: launch_nvfp4<6>(a, st); break;
-            case 7: launch_nvfp4<7>(a, st); break;
-            default: launch_nvfp4<8>(a, st); break;
-        }
-    } else {
-        switch (rb) {
-            case 0: launch_int4<0>(a, st); break;
-            case 1: launch_int4<1>(a, st); break;
-            case 2: launch_int4<2>(a, st); break;
-            case 3: launch_int4<3>(a, st); break;
-            case 4: launch_int4<4>(a, st); break;
-            case 5: launch_int4<5>(a, st); break;
-            case 6: launch_int4<6>(a, st); break;
-            case 7: launch_int4<7>(a, st); break;
-            default: launch_int4<8>(a, st); break;
-        }
+    switch (a.r / 16) {
+        case 0: launch_rb<0>(a, st); break;
+        case 1: launch_rb<1>(a, st); break;
+        case 2: launch_rb<2>(a, st); break;
+        case 3: launch_rb<3>(a, st); break;
+        case 4: launch_rb<4>(a, st); break;
+        case 5: launch_rb<5>(a, st); break;
+        case 6: launch_rb<6>(a, st); break;
+        case 7: launch_rb<7>(a, st); break;
+        default: launch_rb<8>(a, st); break;
     }
 }
 

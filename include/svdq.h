@@ -145,6 +145,31 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
                            const void* bias, int32_t out_dtype, void* out,
                            svdq_stream_t stream);
 
+/*
+ * Prepacked INT4 weights -- the fast GEMM path.  A layer's weights are static, so they are
+ * converted once into the GEMM's operand layout ([margrop] 技术细节 1 step 3: the 4-bit
+ * residual weights): every int4 code q as an exact FP6 (E2M3) value q/8 in MFMA lane order,
+ * the per-group weight scales as bf16 hi/lo pairs, and per (row, group) the term
+ * -8 * sw[n,g] * sum_{k in g} qw[n,k] that the GEMM needs for its activation encoding.
+ * The buffer holds 6 bits per weight plus ~0.5 byte per (row, group) of scale data.
+ *
+ * svdq_prepacked_weight_bytes: size in bytes of the prepacked buffer of `cfg` (INT4 only).
+ * svdq_prepack_weight: wgt_codes [N, K/2] (two's-complement nibbles, even channel low) and
+ *   wgt_scales [N, K/64] fp32 (device) -> prepacked (device, svdq_prepacked_weight_bytes
+ *   bytes, 16-byte aligned), enqueued on `stream`.  Weight codes may use the full [-8, 7].
+ * svdq_gemm_w4a4_prepacked: as svdq_gemm_w4a4 (INT4), with the weights in prepacked form.
+ *   act_codes / act_scales as written by svdq_quantize_act.  The result equals the
+ *   unprepacked GEMM's up to fp32 rounding order (relative error well below 1e-4).
+ */
+svdq_status svdq_prepacked_weight_bytes(const svdq_layer_cfg* cfg, int64_t* bytes);
+svdq_status svdq_prepack_weight(const svdq_layer_cfg* cfg, const void* wgt_codes,
+                                const void* wgt_scales, void* prepacked, svdq_stream_t stream);
+svdq_status svdq_gemm_w4a4_prepacked(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
+                                     const void* act_scales, const void* prepacked,
+                                     const void* lora_act, const void* l2, const void* bias,
+                                     int32_t act, int32_t out_dtype, void* out,
+                                     svdq_stream_t stream);
+
 /* SVDQ_OK when HIP device `device` is a gfx950 GPU, else SVDQ_ERR_UNSUPPORTED_DEVICE
  * (or SVDQ_ERR_INVALID_ARG for a bad ordinal).  Results are cached per device. */
 svdq_status svdq_check_device(int device);

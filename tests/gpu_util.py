@@ -64,6 +64,33 @@ def gemm(codes, scales, wcodes, wscales, lora=None, l2=None, bias=None, act=0, o
     return out
 
 
+def prepack(wcodes, wscales, K, N):
+    cfg = bd.LayerCfg.make(K, N, 0)
+    nbytes = bd.svdq_prepacked_weight_bytes(cfg)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    wc = wcodes if torch.is_tensor(wcodes) else dev(wcodes)
+    ws = wscales if torch.is_tensor(wscales) else dev(wscales)
+    bd.svdq_prepack_weight(cfg, wc, ws, buf)
+    return buf
+
+
+def gemm_prepacked(codes, scales, packed, N, lora=None, l2=None, bias=None, act=0,
+                   out_bf16=False):
+    M = codes.shape[0]
+    K = codes.shape[1] * 2
+    r = 0 if lora is None else lora.shape[1]
+    l2d = None if l2 is None or r == 0 else (l2 if torch.is_tensor(l2) else dev(l2))
+    bd_ = None if bias is None else (bias if torch.is_tensor(bias) else dev(bias))
+    lo = None if r == 0 else (lora if torch.is_tensor(lora) else dev(lora))
+    cfg = bd.LayerCfg.make(K, N, r)
+    out = empty((M, N), np.uint16 if out_bf16 else np.float32)
+    c = codes if torch.is_tensor(codes) else dev(codes)
+    s = scales if torch.is_tensor(scales) else dev(scales)
+    bd.svdq_gemm_w4a4_prepacked(cfg, M, c, s, packed, lo, l2d, bd_, act,
+                                bd.SVDQ_DT_BF16 if out_bf16 else bd.SVDQ_DT_F32, out)
+    return out
+
+
 def awq(x_bf16, q, sc, z, bias=None, out_bf16=False):
     x = x_bf16 if torch.is_tensor(x_bf16) else dev(x_bf16)
     M, K = x.shape
