@@ -89,7 +89,7 @@ def make_inputs(copies):
             l1=t16(synth.random_bf16(rng, (R, K), 0.02)),
             l2=t16(synth.random_bf16(rng, (N, R), 0.02)),
             bias=t16(d.bias_bf16),
-            codes=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+            apacked=torch.empty(bd.svdq_act_packed_bytes(cfg_w, M), dtype=torch.uint8, device=dev),
             scales=torch.empty((M, K // 64), dtype=torch.float32, device=dev),
             lora=torch.empty((M, R), dtype=torch.int16, device=dev),
             out=torch.empty((M, N), dtype=torch.int16, device=dev),
@@ -140,14 +140,16 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
+    def quant(s):
+        bd.svdq_quantize_act_packed(cfg, M, s["x"], si, s["l1"], s["apacked"], s["scales"],
+                                    s["lora"], sp)
+
     def gemm(s):
-        bd.svdq_gemm_w4a4_prepacked(cfg, M, s["codes"], s["scales"], s["packed"], s["lora"],
-                                    s["l2"], s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16,
-                                    s["out"], sp)
+        bd.svdq_gemm_w4a4_packed(cfg, M, s["apacked"], s["packed"], s["lora"], s["l2"],
+                                 s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16, s["out"], sp)
 
     def step(s):
-        bd.svdq_quantize_act(cfg, M, s["x"], si, s["l1"], 1.0, s["codes"], s["scales"],
-                             s["lora"], sp)
+        quant(s)
         gemm(s)
 
     for i in range(args.warmup):
@@ -168,8 +170,7 @@ def main():
     for i in range(args.steps):
         s = sets[i % len(sets)]
         evs[3 * i].record(stream)
-        bd.svdq_quantize_act(cfg, M, s["x"], si, s["l1"], 1.0, s["codes"], s["scales"],
-                             s["lora"], sp)
+        quant(s)
         evs[3 * i + 1].record(stream)
         gemm(s)
         evs[3 * i + 2].record(stream)
@@ -181,7 +182,10 @@ def main():
     ops_total = ops_gemm + 2.0 * M * K * R
     value = ops_total / (ms_step * 1e-3) / 1e12
     gemm_tops = ops_gemm / (t_g.mean() * 1e-3) / 1e12
-    quant_bytes = M * K * 2 + K * 4 + R * K * 2 + M * K // 2 + M * (K // 64) * 4 + M * R * 2
+    # read x, smooth_inv, L1; write 6-bit codes + a 4-byte scale word per (row, group), the
+    # fp32 scales and lora_act
+    quant_bytes = (M * K * 2 + K * 4 + R * K * 2 + M * K * 3 // 4 + M * (K // 64) * 8
+                   + M * R * 2)
     quant_gbs = quant_bytes / (t_q.mean() * 1e-3) / 1e9
 
     out = {
@@ -202,7 +206,7 @@ def main():
                    round(100 * value / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": None, "kernel": "svdq_gemm_w4a4_prepacked (int4, FP6 MFMA)",
+                     "traffic": None, "kernel": "svdq_gemm_w4a4_packed (int4 as FP6 on the MFMA)",
                      "ms_per_launch": round(float(t_g.mean()), 5)},
         "kernels": {
             "quantize_act_ms": round(float(t_q.mean()), 5),

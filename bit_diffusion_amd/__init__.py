@@ -17,7 +17,8 @@ from ._abi import (SVDQ_OK, SVDQ_ERR_INVALID_ARG, SVDQ_ERR_UNSUPPORTED_DEVICE,  
 
 __all__ = [
     "svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_device",
-    "svdq_prepacked_weight_bytes", "svdq_prepack_weight", "svdq_gemm_w4a4_prepacked",
+    "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
+    "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -72,10 +73,28 @@ def awq_gemm_w4a16(M, K, N, group_size, x, qweight, scales, zeros, bias, out_dty
                                    int(out_dtype), _ptr(out), _stream(stream)))
 
 
+def svdq_act_packed_bytes(cfg, M):
+    n = ctypes.c_int64(0)
+    _check(lib().svdq_act_packed_bytes(ctypes.byref(cfg), int(M), ctypes.byref(n)))
+    return n.value
+
+
 def svdq_prepacked_weight_bytes(cfg):
     n = ctypes.c_int64(0)
     _check(lib().svdq_prepacked_weight_bytes(ctypes.byref(cfg), ctypes.byref(n)))
     return n.value
+
+
+def svdq_quantize_act_packed(cfg, M, x, smooth_inv, l1, act_packed, act_scales, lora_act,
+                             stream=None):
+    return _check(lib().svdq_quantize_act_packed(
+        ctypes.byref(cfg), int(M), _ptr(x), _ptr(smooth_inv), _ptr(l1), _ptr(act_packed),
+        _ptr(act_scales), _ptr(lora_act), _stream(stream)))
+
+
+def svdq_pack_act(cfg, M, act_codes, act_scales, act_packed, stream=None):
+    return _check(lib().svdq_pack_act(ctypes.byref(cfg), int(M), _ptr(act_codes),
+                                      _ptr(act_scales), _ptr(act_packed), _stream(stream)))
 
 
 def svdq_prepack_weight(cfg, wgt_codes, wgt_scales, prepacked, stream=None):
@@ -83,12 +102,11 @@ def svdq_prepack_weight(cfg, wgt_codes, wgt_scales, prepacked, stream=None):
                                             _ptr(prepacked), _stream(stream)))
 
 
-def svdq_gemm_w4a4_prepacked(cfg, M, act_codes, act_scales, prepacked, lora_act, l2, bias, act,
-                             out_dtype, out, stream=None):
-    return _check(lib().svdq_gemm_w4a4_prepacked(
-        ctypes.byref(cfg), int(M), _ptr(act_codes), _ptr(act_scales), _ptr(prepacked),
-        _ptr(lora_act), _ptr(l2), _ptr(bias), int(act), int(out_dtype), _ptr(out),
-        _stream(stream)))
+def svdq_gemm_w4a4_packed(cfg, M, act_packed, prepacked, lora_act, l2, bias, act, out_dtype, out,
+                          stream=None):
+    return _check(lib().svdq_gemm_w4a4_packed(
+        ctypes.byref(cfg), int(M), _ptr(act_packed), _ptr(prepacked), _ptr(lora_act), _ptr(l2),
+        _ptr(bias), int(act), int(out_dtype), _ptr(out), _stream(stream)))
 
 
 def svdq_check_device(device=0):

@@ -24,7 +24,8 @@ SVDQ_ACT_GELU_TANH = 1
 # Every symbol include/svdq.h declares.
 EXPORTS = ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_device",
            "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version",
-           "svdq_prepacked_weight_bytes", "svdq_prepack_weight", "svdq_gemm_w4a4_prepacked")
+           "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
+           "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed")
 
 
 class LayerCfg(ctypes.Structure):
@@ -63,9 +64,12 @@ def lib():
         L.svdq_quantize_act.argtypes = [cfgp, I64, P, P, P, F, P, P, P, P]
         L.svdq_gemm_w4a4.argtypes = [cfgp, I64, P, P, F, P, P, F, P, P, P, I32, I32, P, P]
         L.awq_gemm_w4a16.argtypes = [I64, I32, I32, I32, P, P, P, P, P, I32, P, P]
+        L.svdq_act_packed_bytes.argtypes = [cfgp, I64, ctypes.POINTER(ctypes.c_int64)]
         L.svdq_prepacked_weight_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_int64)]
+        L.svdq_quantize_act_packed.argtypes = [cfgp, I64, P, P, P, P, P, P, P]
+        L.svdq_pack_act.argtypes = [cfgp, I64, P, P, P, P]
         L.svdq_prepack_weight.argtypes = [cfgp, P, P, P, P]
-        L.svdq_gemm_w4a4_prepacked.argtypes = [cfgp, I64, P, P, P, P, P, P, I32, I32, P, P]
+        L.svdq_gemm_w4a4_packed.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P]
         L.svdq_check_device.argtypes = [ctypes.c_int]
         L.svdq_check_arch.argtypes = [ctypes.c_char_p]
         L.svdq_status_string.argtypes = [ctypes.c_int]
@@ -74,8 +78,9 @@ def lib():
         L.svdq_last_error.restype = ctypes.c_char_p
         L.svdq_version.restype = ctypes.c_int32
         for name in ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16",
-                     "svdq_check_device", "svdq_check_arch", "svdq_prepacked_weight_bytes",
-                     "svdq_prepack_weight", "svdq_gemm_w4a4_prepacked"):
+                     "svdq_check_device", "svdq_check_arch", "svdq_act_packed_bytes",
+                     "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed", "svdq_pack_act",
+                     "svdq_prepack_weight", "svdq_gemm_w4a4_packed"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

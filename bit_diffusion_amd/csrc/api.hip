@@ -17,6 +17,7 @@
 
 #include "../../include/svdq.h"
 #include "launch.hpp"
+#include "packed_layout.hpp"
 
 namespace {
 
@@ -96,6 +97,12 @@ svdq_status check_cfg(const svdq_layer_cfg* cfg) {
     return SVDQ_OK;
 }
 
+svdq_status check_int4(const svdq_layer_cfg* cfg) {
+    if (cfg->precision != SVDQ_PREC_INT4)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "packed operands exist for INT4 only");
+    return SVDQ_OK;
+}
+
 svdq_status check_global_scale(float s, const char* name) {
     if (!(std::isfinite(s) && s > 0.0f))
         return fail(SVDQ_ERR_INVALID_ARG, "%s = %g must be finite and positive", name, (double)s);
@@ -142,8 +149,8 @@ svdq_status svdq_quantize_act(const svdq_layer_cfg* cfg, int64_t M, const void* 
                     "(4 * (K + 2048 * rank / 16) bytes <= 160 KiB)", cfg->in_features, cfg->rank);
     SVDQ_TRY(check_current_device());
     if (M == 0) return SVDQ_OK;
-    svdq::QuantArgs a{M, cfg->in_features, cfg->rank, nvfp4, x, smooth_inv, l1, act_global_scale,
-                      act_codes, act_scales, lora_act};
+    svdq::QuantArgs a{M, cfg->in_features, cfg->rank, nvfp4 ? 2 : 0, x, smooth_inv, l1,
+                      act_global_scale, act_codes, act_scales, lora_act};
     svdq::launch_quantize_act(a, reinterpret_cast<hipStream_t>(stream));
     return after_launch("svdq_quantize_act");
 }
@@ -208,44 +215,98 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
     return after_launch("awq_gemm_w4a16");
 }
 
+svdq_status svdq_act_packed_bytes(const svdq_layer_cfg* cfg, int64_t M, int64_t* bytes) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    if (bytes == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "bytes is NULL");
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    *bytes = svdq::packed::act_bytes(M, cfg->in_features);
+    return SVDQ_OK;
+}
+
 svdq_status svdq_prepacked_weight_bytes(const svdq_layer_cfg* cfg, int64_t* bytes) {
     SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
     if (bytes == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "bytes is NULL");
-    if (cfg->precision != SVDQ_PREC_INT4)
-        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "prepacked weights exist for INT4 only");
-    *bytes = svdq::prepacked_int4_bytes(cfg->out_features, cfg->in_features);
+    *bytes = svdq::packed::wgt_bytes(cfg->out_features, cfg->in_features);
     return SVDQ_OK;
+}
+
+svdq_status svdq_quantize_act_packed(const svdq_layer_cfg* cfg, int64_t M, const void* x,
+                                     const float* smooth_inv, const void* l1, void* act_packed,
+                                     float* act_scales, void* lora_act, svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    SVDQ_TRY(check_ptr(x, "x", 16));
+    SVDQ_TRY(check_ptr(smooth_inv, "smooth_inv", 16));
+    SVDQ_TRY(check_ptr(act_packed, "act_packed", 16));
+    if (act_scales != nullptr && !aligned(act_scales, 4))
+        return fail(SVDQ_ERR_INVALID_ARG, "act_scales is not 4-byte aligned");
+    if (cfg->rank > 0) {
+        SVDQ_TRY(check_ptr(l1, "l1", 16));
+        SVDQ_TRY(check_ptr(lora_act, "lora_act", 16));
+    }
+    if (M > (int64_t)1 << 35)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
+    if (svdq::quantize_act_lds_bytes(cfg->in_features, cfg->rank) > 160 * 1024)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG,
+                    "in_features %d with rank %d exceeds the activation kernel's LDS budget "
+                    "(4 * (K + 2048 * rank / 16) bytes <= 160 KiB)", cfg->in_features, cfg->rank);
+    SVDQ_TRY(check_current_device());
+    if (M == 0) return SVDQ_OK;
+    svdq::QuantArgs a{M, cfg->in_features, cfg->rank, 1, x, smooth_inv, l1, 1.0f, act_packed,
+                      act_scales, lora_act};
+    svdq::launch_quantize_act(a, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_quantize_act_packed");
+}
+
+svdq_status svdq_pack_act(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
+                          const float* act_scales, void* act_packed, svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    SVDQ_TRY(check_ptr(act_codes, "act_codes", 16));
+    SVDQ_TRY(check_ptr(act_scales, "act_scales", 4));
+    SVDQ_TRY(check_ptr(act_packed, "act_packed", 16));
+    const int64_t blocks = (M + 255) / 256 * 8 * (int64_t)(cfg->in_features / 64);
+    if (blocks >= (int64_t)1 << 31)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
+    SVDQ_TRY(check_current_device());
+    if (M == 0) return SVDQ_OK;
+    svdq::launch_pack_act(M, cfg->in_features, act_codes, act_scales, act_packed,
+                          reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_pack_act");
 }
 
 svdq_status svdq_prepack_weight(const svdq_layer_cfg* cfg, const void* wgt_codes,
                                 const void* wgt_scales, void* prepacked, svdq_stream_t stream) {
     SVDQ_TRY(check_cfg(cfg));
-    if (cfg->precision != SVDQ_PREC_INT4)
-        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "prepacked weights exist for INT4 only");
+    SVDQ_TRY(check_int4(cfg));
     SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", 16));
     SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", 4));
     SVDQ_TRY(check_ptr(prepacked, "prepacked", 16));
+    const int64_t blocks = (int64_t)(cfg->out_features + 191) / 192 * 6 * (cfg->in_features / 64);
+    if (blocks >= (int64_t)1 << 31)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "layer too large for one launch");
     SVDQ_TRY(check_current_device());
-    svdq::launch_prepack_int4(cfg->out_features, cfg->in_features, wgt_codes, wgt_scales, prepacked,
-                              reinterpret_cast<hipStream_t>(stream));
+    svdq::launch_prepack_wgt(cfg->out_features, cfg->in_features, wgt_codes, wgt_scales, prepacked,
+                             reinterpret_cast<hipStream_t>(stream));
     return after_launch("svdq_prepack_weight");
 }
 
-svdq_status svdq_gemm_w4a4_prepacked(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
-                                     const void* act_scales, const void* prepacked,
-                                     const void* lora_act, const void* l2, const void* bias,
-                                     int32_t act, int32_t out_dtype, void* out,
-                                     svdq_stream_t stream) {
+svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
+                                  const void* prepacked, const void* lora_act, const void* l2,
+                                  const void* bias, int32_t act, int32_t out_dtype, void* out,
+                                  svdq_stream_t stream) {
     SVDQ_TRY(check_cfg(cfg));
-    if (cfg->precision != SVDQ_PREC_INT4)
-        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "prepacked weights exist for INT4 only");
+    SVDQ_TRY(check_int4(cfg));
     if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
     if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
         return fail(SVDQ_ERR_INVALID_ARG, "act %d is not a svdq_act value", act);
     if (out_dtype != SVDQ_DT_F32 && out_dtype != SVDQ_DT_BF16)
         return fail(SVDQ_ERR_INVALID_ARG, "out_dtype %d is not a svdq_dtype value", out_dtype);
-    SVDQ_TRY(check_ptr(act_codes, "act_codes", 16));
-    SVDQ_TRY(check_ptr(act_scales, "act_scales", 4));
+    SVDQ_TRY(check_ptr(act_packed, "act_packed", 16));
     SVDQ_TRY(check_ptr(prepacked, "prepacked", 16));
     SVDQ_TRY(check_ptr(out, "out", out_dtype == SVDQ_DT_F32 ? 4 : 2));
     if (cfg->rank > 0) {
@@ -254,18 +315,16 @@ svdq_status svdq_gemm_w4a4_prepacked(const svdq_layer_cfg* cfg, int64_t M, const
     }
     if (bias != nullptr && !aligned(bias, 2)) return fail(SVDQ_ERR_INVALID_ARG, "bias is not 2-byte aligned");
     const int64_t tiles = ((M + 255) / 256) * ((cfg->out_features + 191) / 192);
-    if (tiles > (int64_t)1 << 30)
+    if (tiles >= (int64_t)1 << 31)
         return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
     SVDQ_TRY(check_current_device());
     if (M == 0) return SVDQ_OK;
-    if (!svdq::gemm_int4_fp6_init())
-        return fail(SVDQ_ERR_LAUNCH, "could not reserve LDS for the prepacked GEMM");
-    svdq::PrepackedGemmArgs a{M, cfg->out_features, cfg->in_features, cfg->rank,
-                              svdq::prepacked_ntiles_padded(cfg->out_features), act_codes,
-                              act_scales, prepacked, lora_act, l2, bias, act,
-                              out_dtype == SVDQ_DT_BF16 ? 1 : 0, out};
-    svdq::launch_gemm_int4_fp6(a, reinterpret_cast<hipStream_t>(stream));
-    return after_launch("svdq_gemm_w4a4_prepacked");
+    if (!svdq::gemm_w4a4_fp6_init())
+        return fail(SVDQ_ERR_LAUNCH, "could not reserve LDS for the packed GEMM");
+    svdq::PackedGemmArgs a{M, cfg->out_features, cfg->in_features, cfg->rank, act_packed,
+                           prepacked, lora_act, l2, bias, act, out_dtype == SVDQ_DT_BF16 ? 1 : 0, out, 0};
+    svdq::launch_gemm_w4a4_fp6(a, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_gemm_w4a4_packed");
 }
 
 svdq_status svdq_check_device(int device) { return check_device_ordinal(device); }

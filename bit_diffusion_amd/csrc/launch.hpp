@@ -9,13 +9,13 @@ namespace svdq {
 struct QuantArgs {
     int64_t M;
     int K, r;
-    bool nvfp4;
+    int mode;       // 0 INT4 nibbles, 1 INT4 packed (packed_layout.hpp), 2 NVFP4 nibbles
     const void* x;
     const float* smooth_inv;
     const void* l1;
     float S;
-    void* codes;
-    void* scales;
+    void* codes;    // nibbles, or the packed activation buffer in mode 1
+    void* scales;   // may be NULL in mode 1
     void* lora;
 };
 
@@ -49,19 +49,18 @@ struct AwqArgs {
     void* out;
 };
 
-struct PrepackedGemmArgs {
+struct PackedGemmArgs {
     int64_t M;
     int N, K, r;
-    int ntiles_padded;
-    const void* acodes;
-    const void* ascales;
-    const void* prepacked;
+    const void* act;   // packed activations
+    const void* wgt;   // packed weights
     const void* lora;
     const void* l2;
     const void* bias;
-    int act;
+    int act_fn;
     int out_bf16;
     void* out;
+    int vec_store;     // set by the launcher
 };
 
 size_t quantize_act_lds_bytes(int K, int r);
@@ -70,11 +69,11 @@ void launch_gemm_int4(const GemmArgs& a, hipStream_t st);
 void launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);
 void launch_awq_gemv(const AwqArgs& a, hipStream_t st);
 
-int64_t prepacked_int4_bytes(int N, int K);
-int prepacked_ntiles_padded(int N);
-void launch_prepack_int4(int N, int K, const void* wcodes, const void* wscales, void* out,
-                         hipStream_t st);
-bool gemm_int4_fp6_init();
-void launch_gemm_int4_fp6(const PrepackedGemmArgs& a, hipStream_t st);
+void launch_prepack_wgt(int N, int K, const void* wcodes, const void* wscales, void* out,
+                        hipStream_t st);
+void launch_pack_act(int64_t M, int K, const void* acodes, const void* ascales, void* out,
+                     hipStream_t st);
+bool gemm_w4a4_fp6_init();
+void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st);
 
 }  // namespace svdq

@@ -138,7 +138,8 @@ svdq_status svdq_gemm_w4a4(const svdq_layer_cfg* cfg, int64_t M, const void* act
  *   bias     [N] bf16 or NULL.
  *   out      [M, N] fp32 or bf16: y = sum_k x[m,k] (q[n,k] - z[n,g]) s[n,g] + bias[n],
  *            accumulated in fp32.
- * group_size must be 64; K a multiple of 64; M <= 64.
+ * group_size must be 64; K a multiple of 64; any M >= 0 (one pass over the weights
+ * serves up to 4 rows; larger M re-reads them).
  */
 svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, const void* x,
                            const void* qweight, const void* scales, const void* zeros,
@@ -146,29 +147,43 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
                            svdq_stream_t stream);
 
 /*
- * Prepacked INT4 weights -- the fast GEMM path.  A layer's weights are static, so they are
- * converted once into the GEMM's operand layout ([margrop] 技术细节 1 step 3: the 4-bit
- * residual weights): every int4 code q as an exact FP6 (E2M3) value q/8 in MFMA lane order,
- * the per-group weight scales as bf16 hi/lo pairs, and per (row, group) the term
- * -8 * sw[n,g] * sum_{k in g} qw[n,k] that the GEMM needs for its activation encoding.
- * The buffer holds 6 bits per weight plus ~0.5 byte per (row, group) of scale data.
+ * Packed INT4 operands -- the fast GEMM path ([margrop] 技术细节 1 steps 3-4: the quantize
+ * kernel hands the GEMM its 4-bit operands in the layout the matrix unit consumes).
+ * Both operands are stored as exact FP6 (E2M3) values q/8 of the int4 codes in the lane
+ * order of the gfx950 32x32x64 FP6 MFMA, 32 rows (or columns) x 64 channels per fragment,
+ * each followed by the group scales as bf16 hi/lo pairs (hi = bf16(s), lo = bf16(s - hi)).
+ * Activations take 6 bits per code plus 4 bytes per (row, group) and are padded to a
+ * multiple of 256 rows; weights take 6 bits per code plus 16 bytes per (column, group) and
+ * are padded to a multiple of 192 columns.  The buffers are opaque; sizes come from the
+ * *_bytes queries.  All buffers are device memory, 16-byte aligned, owned by the caller.
  *
- * svdq_prepacked_weight_bytes: size in bytes of the prepacked buffer of `cfg` (INT4 only).
- * svdq_prepack_weight: wgt_codes [N, K/2] (two's-complement nibbles, even channel low) and
- *   wgt_scales [N, K/64] fp32 (device) -> prepacked (device, svdq_prepacked_weight_bytes
- *   bytes, 16-byte aligned), enqueued on `stream`.  Weight codes may use the full [-8, 7].
- * svdq_gemm_w4a4_prepacked: as svdq_gemm_w4a4 (INT4), with the weights in prepacked form.
- *   act_codes / act_scales as written by svdq_quantize_act.  The result equals the
- *   unprepacked GEMM's up to fp32 rounding order (relative error well below 1e-4).
+ * svdq_act_packed_bytes / svdq_prepacked_weight_bytes: buffer sizes for `cfg` (INT4 only)
+ *   and M rows.
+ * svdq_quantize_act_packed: as svdq_quantize_act (INT4), writing the codes into act_packed
+ *   instead of nibbles; the codes, the fp32 scales (act_scales, may be NULL) and lora_act
+ *   are bit-identical to svdq_quantize_act's.  Padding rows of act_packed are zero.
+ * svdq_pack_act: act_codes [M, K/2] nibbles + act_scales [M, K/64] fp32 (svdq_quantize_act
+ *   output) -> act_packed.
+ * svdq_prepack_weight: wgt_codes [N, K/2] nibbles (full range [-8, 7]) + wgt_scales
+ *   [N, K/64] fp32 -> prepacked, once per layer.
+ * svdq_gemm_w4a4_packed: as svdq_gemm_w4a4 (INT4) on packed operands.  The result equals
+ *   svdq_gemm_w4a4's up to fp32 rounding order and the hi/lo split of each scale product
+ *   (relative error of one group's term below 2^-15).
+ * All enqueue on `stream`.
  */
+svdq_status svdq_act_packed_bytes(const svdq_layer_cfg* cfg, int64_t M, int64_t* bytes);
 svdq_status svdq_prepacked_weight_bytes(const svdq_layer_cfg* cfg, int64_t* bytes);
+svdq_status svdq_quantize_act_packed(const svdq_layer_cfg* cfg, int64_t M, const void* x,
+                                     const float* smooth_inv, const void* l1, void* act_packed,
+                                     float* act_scales, void* lora_act, svdq_stream_t stream);
+svdq_status svdq_pack_act(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
+                          const float* act_scales, void* act_packed, svdq_stream_t stream);
 svdq_status svdq_prepack_weight(const svdq_layer_cfg* cfg, const void* wgt_codes,
                                 const void* wgt_scales, void* prepacked, svdq_stream_t stream);
-svdq_status svdq_gemm_w4a4_prepacked(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
-                                     const void* act_scales, const void* prepacked,
-                                     const void* lora_act, const void* l2, const void* bias,
-                                     int32_t act, int32_t out_dtype, void* out,
-                                     svdq_stream_t stream);
+svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
+                                  const void* prepacked, const void* lora_act, const void* l2,
+                                  const void* bias, int32_t act, int32_t out_dtype, void* out,
+                                  svdq_stream_t stream);
 
 /* SVDQ_OK when HIP device `device` is a gfx950 GPU, else SVDQ_ERR_UNSUPPORTED_DEVICE
  * (or SVDQ_ERR_INVALID_ARG for a bad ordinal).  Results are cached per device. */

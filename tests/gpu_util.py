@@ -74,21 +74,97 @@ def prepack(wcodes, wscales, K, N):
     return buf
 
 
-def gemm_prepacked(codes, scales, packed, N, lora=None, l2=None, bias=None, act=0,
-                   out_bf16=False):
-    M = codes.shape[0]
-    K = codes.shape[1] * 2
+def act_packed_bytes(M, K):
+    return bd.svdq_act_packed_bytes(bd.LayerCfg.make(K, 1, 0), M)
+
+
+def pack_act(codes, scales, K):
+    """svdq_pack_act: nibble codes + fp32 scales -> packed activation buffer."""
+    c = codes if torch.is_tensor(codes) else dev(codes)
+    s = scales if torch.is_tensor(scales) else dev(scales)
+    M = c.shape[0]
+    buf = torch.empty(act_packed_bytes(M, K), dtype=torch.uint8, device="cuda:0")
+    bd.svdq_pack_act(bd.LayerCfg.make(K, 1, 0), M, c, s, buf)
+    return buf
+
+
+def quantize_packed(x_bf16, smooth_inv, l1=None, N=1, with_scales=True):
+    """svdq_quantize_act_packed -> (packed buffer, fp32 scales or None, lora) tensors."""
+    x = x_bf16 if torch.is_tensor(x_bf16) else dev(x_bf16)
+    M, K = x.shape
+    r = 0 if l1 is None else l1.shape[0]
+    cfg = bd.LayerCfg.make(K, N, r)
+    buf = torch.empty(act_packed_bytes(M, K), dtype=torch.uint8, device="cuda:0")
+    scales = empty((M, K // 64), np.float32) if with_scales else None
+    lora = empty((M, r), np.uint16) if r else None
+    si = smooth_inv if torch.is_tensor(smooth_inv) else dev(np.asarray(smooth_inv, np.float32))
+    l1d = None if l1 is None else (l1 if torch.is_tensor(l1) else dev(l1))
+    bd.svdq_quantize_act_packed(cfg, M, x, si, l1d, buf, scales, lora)
+    return buf, scales, lora
+
+
+def gemm_packed(apacked, wpacked, M, K, N, lora=None, l2=None, bias=None, act=0, out_bf16=False):
     r = 0 if lora is None else lora.shape[1]
     l2d = None if l2 is None or r == 0 else (l2 if torch.is_tensor(l2) else dev(l2))
     bd_ = None if bias is None else (bias if torch.is_tensor(bias) else dev(bias))
     lo = None if r == 0 else (lora if torch.is_tensor(lora) else dev(lora))
     cfg = bd.LayerCfg.make(K, N, r)
     out = empty((M, N), np.uint16 if out_bf16 else np.float32)
-    c = codes if torch.is_tensor(codes) else dev(codes)
-    s = scales if torch.is_tensor(scales) else dev(scales)
-    bd.svdq_gemm_w4a4_prepacked(cfg, M, c, s, packed, lo, l2d, bd_, act,
-                                bd.SVDQ_DT_BF16 if out_bf16 else bd.SVDQ_DT_F32, out)
+    bd.svdq_gemm_w4a4_packed(cfg, M, apacked, wpacked, lo, l2d, bd_, act,
+                             bd.SVDQ_DT_BF16 if out_bf16 else bd.SVDQ_DT_F32, out)
     return out
+
+
+def gemm_prepacked(codes, scales, packed, N, lora=None, l2=None, bias=None, act=0,
+                   out_bf16=False):
+    """Nibble activations -> svdq_pack_act -> svdq_gemm_w4a4_packed."""
+    M = codes.shape[0]
+    K = codes.shape[1] * 2
+    return gemm_packed(pack_act(codes, scales, K), packed, M, K, N, lora, l2, bias, act,
+                       out_bf16)
+
+
+def _fp6_fields(dw):
+    """[..., 6] uint32 dwords -> [..., 32] six-bit fields (field j at bit 6 j)."""
+    dw = dw.astype(np.uint64)
+    out = np.empty(dw.shape[:-1] + (32,), np.int64)
+    for j in range(32):
+        pos = 6 * j
+        d, o = pos // 32, pos % 32
+        f = dw[..., d] >> np.uint64(o)
+        if o > 26:
+            f = f | (dw[..., d + 1] << np.uint64(32 - o))
+        out[..., j] = (f & np.uint64(63)).astype(np.int64)
+    return out
+
+
+def decode_act_packed(buf, M, K):
+    """Host-side reader of the packed activation layout (test infrastructure): returns the
+    int codes [Mp, K], the scale words (hi | lo << 16) [Mp, G] and a flag that every field
+    is canonical (no negative zero, magnitude <= 8)."""
+    G = K // 64
+    mb = (M + 255) // 256
+    b = np.ascontiguousarray(np.asarray(buf, np.uint8)).reshape(mb, G, 8, 1664)
+    p0 = np.ascontiguousarray(b[..., :1024]).view(np.uint32).reshape(mb, G, 8, 64, 4)
+    p1 = np.ascontiguousarray(b[..., 1024:1536]).view(np.uint32).reshape(mb, G, 8, 64, 2)
+    f = _fp6_fields(np.concatenate([p0, p1], axis=-1))          # mb, G, rb, lane, j
+    mag, neg = f & 31, f >> 5
+    canonical = bool(np.all(mag <= 8) and not np.any((mag == 0) & (neg == 1)))
+    q = np.where(neg == 1, -mag, mag).reshape(mb, G, 8, 2, 32, 32)  # lane = r + 32 h
+    codes = q.transpose(0, 2, 4, 1, 3, 5).reshape(mb * 256, K)
+    words = np.ascontiguousarray(b[..., 1536:]).view(np.uint32).reshape(mb, G, 8, 32)
+    words = words.transpose(0, 2, 3, 1).reshape(mb * 256, G)
+    return codes, words, canonical
+
+
+def split_words(scales):
+    """(hi | lo << 16) with hi = bf16(s), lo = bf16(s - hi), as the packed layout stores."""
+    import synth
+    s = np.asarray(scales, np.float32)
+    hi = synth.f32_to_bf16_bits(s).astype(np.uint32)
+    rest = (s - (hi << 16).view(np.float32)).astype(np.float32)
+    lo = synth.f32_to_bf16_bits(rest).astype(np.uint32)
+    return hi | (lo << 16)
 
 
 def awq(x_bf16, q, sc, z, bias=None, out_bf16=False):

@@ -141,3 +141,91 @@ def test_awq_modulation_gemv(workload_cache):
     yb = gu.host(gu.awq(A["x_prime"], A["qweight"], A["scales"], A["zeros"], A["bias"],
                         out_bf16=True))
     gu.assert_bf16_close(yb, ref)
+
+
+def _quant_packed_exact(xb, L):
+    """GPU fused quantize-and-pack vs oracle on the same input: codes read back from the
+    packed buffer and fp32 scales bit-exact, lora_act within its bound."""
+    M, K = xb.shape
+    buf, scales, lora = gu.quantize_packed(xb, L["smooth_inv"], L["l1"])
+    torch.cuda.synchronize()
+    oc, os_, ol = oracle.quant_act_int4(xb, L["smooth_inv"], L["l1"])
+    q, words, canonical = gu.decode_act_packed(gu.host(buf), M, K)
+    assert canonical
+    assert np.array_equal(q[:M], oracle.unpack_int4(oc).astype(np.int64)), "codes differ"
+    assert np.array_equal(gu.host(scales).view(np.uint32), os_.view(np.uint32)), "scales differ"
+    assert np.array_equal(words[:M], gu.split_words(os_)), "scale words differ"
+    gu.assert_lora_close(gu.host(lora), ol, xb, L["l1"])
+    return (buf, lora), (oc, os_, ol)
+
+
+def test_attn_projection_packed(workload_cache):
+    """The benchmark's path: svdq_quantize_act_packed + svdq_gemm_w4a4_packed."""
+    d, (L,) = _get(workload_cache, 1)
+    M, K = d.x_bf16.shape
+    N = L["wcodes"].shape[0]
+    (buf, gl), (oc, os_, ol) = _quant_packed_exact(d.x_bf16, L)
+    wp = gu.prepack(L["wcodes"], L["wscales"], K, N)
+    rng = np.random.default_rng(11)
+    # GEMM stage on the oracle's activation-stage outputs
+    ap = gu.pack_act(oc, os_, K)
+    for out_bf16 in (False, True):
+        y = gu.host(gu.gemm_packed(ap, wp, M, K, N, ol, L["l2"], L["bias"], out_bf16=out_bf16))
+        mi, ni = _samples(rng, M, N)
+        ref = oracle.gemm_w4a4_int4_at(mi, ni, oc, os_, L["wcodes"], L["wscales"], ol, L["l2"],
+                                       L["bias"])
+        if out_bf16:
+            gu.assert_bf16_close(y[mi, ni], ref)
+        else:
+            e = gu.rel_fro(y[mi, ni], ref)
+            print(f"attn packed gemm rel_fro={e:.3e}")
+            assert e <= 1e-3
+    # end to end: GPU chain vs oracle chain from the same X
+    ye = gu.host(gu.gemm_packed(buf, wp, M, K, N, gl, L["l2"], L["bias"], out_bf16=True))
+    ref = oracle.gemm_w4a4_int4_at(mi, ni, oc, os_, L["wcodes"], L["wscales"], ol, L["l2"],
+                                   L["bias"])
+    got = (ye[mi, ni].astype(np.uint32) << 16).view(np.float32)
+    e2e = gu.rel_fro(got, ref)
+    print(f"attn packed end-to-end (bf16 out) rel_fro={e2e:.3e}")
+    assert e2e <= 1e-3
+
+
+def test_mlp_pair_packed(workload_cache):
+    """fc1 (GELU, bf16 out) and fc2 (K = 12288) on the packed path."""
+    d, (L1, L2) = _get(workload_cache, 2)
+    M, K1 = d.x_bf16.shape
+    N1 = L1["wcodes"].shape[0]
+    N2 = L2["wcodes"].shape[0]
+    rng = np.random.default_rng(12)
+    (b1, gl1), (oc1, os1, ol1) = _quant_packed_exact(d.x_bf16, L1)
+    wp1 = gu.prepack(L1["wcodes"], L1["wscales"], K1, N1)
+    h_or = gu.host(gu.gemm_packed(gu.pack_act(oc1, os1, K1), wp1, M, K1, N1, ol1, L1["l2"],
+                                  L1["bias"], act=1, out_bf16=True))
+    mi1, ni1 = _samples(rng, M, N1, n_pts=2000)
+    ref1 = oracle.gemm_w4a4_int4_at(mi1, ni1, oc1, os1, L1["wcodes"], L1["wscales"], ol1,
+                                    L1["l2"], L1["bias"], act=1)
+    gu.assert_bf16_close(h_or[mi1, ni1], ref1)
+    # fc2 on its heavy-tailed calibration input: quantize-and-pack exact, GEMM sampled
+    x2 = d.extras["x2_bf16"]
+    _, (oc3, os3, ol3) = _quant_packed_exact(x2, L2)
+    wp2 = gu.prepack(L2["wcodes"], L2["wscales"], L2["wcodes"].shape[1] * 2, N2)
+    y3 = gu.host(gu.gemm_packed(gu.pack_act(oc3, os3, x2.shape[1]), wp2, x2.shape[0],
+                                x2.shape[1], N2, ol3, L2["l2"], L2["bias"]))
+    mi3, ni3 = _samples(rng, *y3.shape, n_pts=2000)
+    ref3 = oracle.gemm_w4a4_int4_at(mi3, ni3, oc3, os3, L2["wcodes"], L2["wscales"], ol3,
+                                    L2["l2"], L2["bias"])
+    e3 = gu.rel_fro(y3[mi3, ni3], ref3)
+    print(f"mlp fc2 packed gemm rel_fro={e3:.3e}")
+    assert e3 <= 1e-3
+    # GPU chain end to end on a few token rows against the oracle chain
+    h = gu.gemm_packed(b1, wp1, M, K1, N1, gl1, L1["l2"], L1["bias"], act=1, out_bf16=True)
+    b2, _, lo2 = gu.quantize_packed(h, L2["smooth_inv"], L2["l1"])
+    y = gu.host(gu.gemm_packed(b2, wp2, M, N1, N2, lo2, L2["l2"], L2["bias"]))
+    rows = np.array([0, 1, 777, 2048, 4095, M - 1])
+    y1 = oracle.gemm_w4a4_int4(oc1[rows], os1[rows], L1["wcodes"], L1["wscales"], ol1[rows],
+                               L1["l2"], L1["bias"], act=1)
+    qc, qs, ql = oracle.quant_act_int4(bf16_from_f64_vec(y1), L2["smooth_inv"], L2["l1"])
+    y2 = oracle.gemm_w4a4_int4(qc, qs, L2["wcodes"], L2["wscales"], ql, L2["l2"], L2["bias"])
+    e2e = gu.rel_fro(y[rows], y2)
+    print(f"mlp packed end-to-end rel_fro={e2e:.3e}")
+    assert e2e <= 1e-3
