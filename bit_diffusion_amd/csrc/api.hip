@@ -143,10 +143,6 @@ svdq_status svdq_quantize_act(const svdq_layer_cfg* cfg, int64_t M, const void* 
     if (nvfp4) SVDQ_TRY(check_global_scale(act_global_scale, "act_global_scale"));
     if (M > (int64_t)1 << 35)
         return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
-    if (svdq::quantize_act_lds_bytes(cfg->in_features, cfg->rank) > 160 * 1024)
-        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG,
-                    "in_features %d with rank %d exceeds the activation kernel's LDS budget "
-                    "(4 * (K + 2048 * rank / 16) bytes <= 160 KiB)", cfg->in_features, cfg->rank);
     SVDQ_TRY(check_current_device());
     if (M == 0) return SVDQ_OK;
     svdq::QuantArgs a{M, cfg->in_features, cfg->rank, nvfp4 ? 2 : 0, x, smooth_inv, l1,
@@ -249,10 +245,6 @@ svdq_status svdq_quantize_act_packed(const svdq_layer_cfg* cfg, int64_t M, const
     }
     if (M > (int64_t)1 << 35)
         return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
-    if (svdq::quantize_act_lds_bytes(cfg->in_features, cfg->rank) > 160 * 1024)
-        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG,
-                    "in_features %d with rank %d exceeds the activation kernel's LDS budget "
-                    "(4 * (K + 2048 * rank / 16) bytes <= 160 KiB)", cfg->in_features, cfg->rank);
     SVDQ_TRY(check_current_device());
     if (M == 0) return SVDQ_OK;
     svdq::QuantArgs a{M, cfg->in_features, cfg->rank, 1, x, smooth_inv, l1, 1.0f, act_packed,

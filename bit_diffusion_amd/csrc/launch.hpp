@@ -63,7 +63,6 @@ struct PackedGemmArgs {
     int vec_store;     // set by the launcher
 };
 
-size_t quantize_act_lds_bytes(int K, int r);
 void launch_quantize_act(const QuantArgs& a, hipStream_t st);
 void launch_gemm_int4(const GemmArgs& a, hipStream_t st);
 void launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);

@@ -10,12 +10,18 @@
 //   * the low-rank down-projection lora_act = X . L1^T on the same registers (bf16 MFMA),
 //     so the 16-bit branch costs no extra pass over X.
 //
-// Work mapping: a block of 16 waves owns 16 token rows; wave w walks groups w, w+16, ...
-// Lane l holds row (l % 16) and the 16 consecutive channels 16 * (l / 16) .. +15 of the
-// current 64-channel group: the A-operand layout of two v_mfma_f32_16x16x32_bf16 (one per
-// 32-channel half) for the low-rank down-projection.  The group absmax is a max over the
-// four lanes of a row (xor-shuffles 16, 32).  Each wave keeps the loads of its next few
-// groups in flight while it processes the current one; smooth_inv sits in LDS.
+// Work mapping: a block of 8 waves owns 16 token rows and walks K in steps of 128 channels
+// (two 64-channel groups); wave w takes steps w, w+8, ...  Lane l holds row l % 16 and the
+// 32 consecutive channels 32 (l / 16) .. +31 of the step, i.e. one half of one group: the
+// lane of one FP6 MFMA fragment, so its 32 codes convert to the fragment's six dwords in a
+// single v_cvt_scalef32_2xpk16_fp6_f32.  The group absmax is a max over the lane's 32
+// values and its partner lane l ^ 16.  For the low-rank down-projection the same registers
+// are the A operands of four v_mfma_f32_16x16x32_bf16 per 16 ranks (the MFMA contracts any
+// consistent permutation of the channels; L1 is loaded in the matching order).
+//
+// A wave issues the loads of up to kAhead steps at once, in straight-line code, so every
+// step waits only for its own data.  smooth_inv goes through a wave-private LDS slice (one
+// 128-float slice per step), which needs no barrier.
 #include "common.hpp"
 #include "launch.hpp"
 #include "packed_layout.hpp"
@@ -28,78 +34,121 @@ namespace {
 
 constexpr int kRows = 16;
 constexpr float kMinNormal = 1.17549435e-38f;
-constexpr int kQWaves = 16;
-constexpr size_t kQuantMaxLds = 160 * 1024;
+constexpr int kQWaves = 8;
 constexpr int kQThreads = kQWaves * 64;
+constexpr int kStep = 128;   // channels per wave step
 
 enum Mode { kInt4Nibbles = 0, kInt4Packed = 1, kNvfp4Nibbles = 2 };
 
-// Up to rank 32 the L1 slices travel with the activations, and two (rank 32) or three
-// (rank <= 16) groups per wave are in flight; beyond that the registers would spill, so one
-// group is in flight and L1 is loaded when it is used.
-template <int RB>
-constexpr bool kPrefetchL1 = RB <= 2;
+// Steps in flight per wave: the register budget (256 VGPRs at 8 waves per block) holds
+// three stages up to rank 16, two at rank 32 and one beyond; above rank 64 the L1 slice is
+// loaded when it is used.
 template <int RB>
 constexpr int kAhead = RB <= 1 ? 3 : RB == 2 ? 2 : 1;
+template <int RB>
+constexpr bool kPrefetchL1 = RB <= 4;
+
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 
 template <int RB>
-struct Stage16 {
-    uint4 xv0, xv1;                                    // 16 bf16 of one row
-    uint4 l1v[kPrefetchL1<RB> && RB > 0 ? 2 * RB : 1]; // L1 rows (16 b + row), this group
+struct Stage {
+    uint4 x[4];                                          // 32 bf16: channels 8t .. 8t+7 in x[t]
+    uint4 l1[kPrefetchL1<RB> && RB > 0 ? 4 * RB : 1];    // L1 row (16 b + l % 16), same channels
 };
 
+__device__ __forceinline__ uint4 load_l1(const uint16_t* l1r, int K, int b, int k0, int t) {
+    return *reinterpret_cast<const uint4*>(l1r + (int64_t)b * 16 * K + k0 + 8 * t);
+}
+
 template <int RB>
-__device__ __forceinline__ void load_stage(Stage16<RB>& st, const uint16_t* xr, const uint16_t* l1,
-                                           int K, int rl, int k0) {
-    st.xv0 = *reinterpret_cast<const uint4*>(xr + k0);
-    st.xv1 = *reinterpret_cast<const uint4*>(xr + k0 + 8);
+__device__ __forceinline__ void load_stage(Stage<RB>& st, const uint16_t* xr, const uint16_t* l1r,
+                                           int K, int k0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) st.x[t] = *reinterpret_cast<const uint4*>(xr + k0 + 8 * t);
     if constexpr (kPrefetchL1<RB>)
 #pragma unroll
-    for (int b = 0; b < RB; ++b) {
-        const uint16_t* lr = l1 + (int64_t)(b * 16 + rl) * K + k0;
-        st.l1v[2 * b] = *reinterpret_cast<const uint4*>(lr);
-        st.l1v[2 * b + 1] = *reinterpret_cast<const uint4*>(lr + 8);
-    }
-}
-
-// x_hat = fp32(x) * smooth_inv for the lane's 16 channels (smooth_inv from LDS); rows
-// beyond M read as zero.
-template <int RB>
-__device__ __forceinline__ void smooth16(float (&xh)[16], const Stage16<RB>& st, const float* si,
-                                         bool valid) {
-    const float4* sp = reinterpret_cast<const float4*>(si);
-    const float4 s4[4] = {sp[0], sp[1], sp[2], sp[3]};
-    const uint32_t w[8] = {st.xv0.x, st.xv0.y, st.xv0.z, st.xv0.w,
-                           st.xv1.x, st.xv1.y, st.xv1.z, st.xv1.w};
+        for (int b = 0; b < RB; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-        xh[i] = valid ? bf16_to_f32(h) * (&s4[i >> 2].x)[i & 3] : 0.0f;
+            for (int t = 0; t < 4; ++t) st.l1[4 * b + t] = load_l1(l1r, K, b, k0, t);
+}
+
+// The lane's 32 values in the order of the FP6 conversion: ev[i] is channel 2i (the low
+// bf16 of word i), od[i] channel 2i + 1 (the high bf16).
+struct Vals {
+    f32x16v ev, od;
+};
+
+// x_hat = fp32(x) * smooth_inv for the lane's 32 channels (smooth_inv from the wave's LDS
+// slice).
+template <int RB>
+__device__ __forceinline__ void smooth32(Vals& v, const Stage<RB>& st, const float* si) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float4 s0 = *reinterpret_cast<const float4*>(si + 8 * t);
+        const float4 s1 = *reinterpret_cast<const float4*>(si + 8 * t + 4);
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const uint32_t w[4] = {st.x[t].x, st.x[t].y, st.x[t].z, st.x[t].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v.ev[4 * t + i] = __uint_as_float(w[i] << 16) * sv[2 * i];
+            v.od[4 * t + i] = __uint_as_float(w[i] & 0xFFFF0000u) * sv[2 * i + 1];
+        }
     }
 }
 
-// rne(xh / s) clamped to [-8, 7] for the lane's 16 values, with the fp32 quotient
-// correctly rounded as the code's definition requires.  The quotient is estimated as
-// xh * (1/s) (within 2^-22 relative of the correctly rounded one, i.e. < 2e-6 for
-// |q| <= 8); only when an estimate lies within 4e-6 of a half-integer can the correctly
-// rounded quotient round differently, and then the lane redoes all 16 with the exact
-// division.  s = 0 (an all-zero group) gives codes 0.
-__device__ __forceinline__ void int4_codes(const float (&xh)[16], float s, float (&q)[16]) {
+// 32 floats -> 32 FP6 E2M3 fields (value / scale, field 2i from ev[i], 2i+1 from od[i]) in
+// six dwords, one v_cvt_scalef32_2xpk16_fp6_f32.  Written as asm with an early-clobber
+// result: the instruction reads its 32 source registers over several cycles, so its six
+// result registers must not overlap them (left to itself the compiler may place them there).
+__device__ __forceinline__ u32x6 cvt_fp6x32(const f32x16v& ev, const f32x16v& od, float scale) {
+    u32x6 r;
+    asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3"
+                 : "=&v"(r) : "v"(ev), "v"(od), "v"(scale));
+    return r;
+}
+
+__device__ __forceinline__ float absmax32(const Vals& v) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fmaxf(fabsf(v.ev[i]), fabsf(v.od[i])));
+    return a;
+}
+
+// rne(xh / s) for the lane's 32 values, in place, with the fp32 quotient correctly rounded
+// as the code's definition requires.  The quotient is estimated as xh * (1/s) (within 2^-22
+// relative of the correctly rounded one, i.e. < 2e-6 for |q| <= 8); only when an estimate
+// lies within 4e-6 of a half-integer can the correctly rounded quotient round differently,
+// and then the lane redoes all 32 with the exact division (smooth32 recomputes x_hat).
+// s = absmax / 7 bounds |xh / s| by 7 (up to rounding), so rne never leaves [-7, 7] and the
+// definition's clamp to [-8, 7] is the identity.  Codes come out as floats with +0 for 0.
+// s = 0 (an all-zero group) gives codes 0.
+__device__ __forceinline__ float rne_keep_d(f32x16v& v, int i, float rcp, float dmax) {
+    const float y = v[i] * rcp;
+    const float d = y - __builtin_rintf(y);
+    v[i] = y - d;   // = rne(y) exactly, with +0 where it is zero
+    return fmaxf(dmax, fabsf(d));
+}
+
+template <int RB>
+__device__ __forceinline__ void int4_codes32(Vals& v, float s, const Stage<RB>& st,
+                                             const float* si) {
     const bool zero = s == 0.0f;
     const float rcp = zero ? 0.0f : 1.0f / s;
-    bool redo = s < kMinNormal && !zero;
+    float dmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const float y = xh[i] * rcp;
-        q[i] = __builtin_rintf(y);
-        redo |= fabsf(y - q[i]) > 0.499996f;
+        dmax = rne_keep_d(v.ev, i, rcp, dmax);
+        dmax = rne_keep_d(v.od, i, rcp, dmax);
     }
-    if (redo && !zero) {
+    if (!zero && (dmax > 0.499996f || s < kMinNormal)) {
+        smooth32<RB>(v, st, si);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) q[i] = __builtin_rintf(xh[i] / s);
+        for (int i = 0; i < 16; ++i) {
+            v.ev[i] = __builtin_rintf(v.ev[i] / s) + 0.0f;
+            v.od[i] = __builtin_rintf(v.od[i] / s) + 0.0f;
+        }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = fminf(fmaxf(q[i], -8.0f), 7.0f);
 }
 
 // Nearest E4M3 ("FN": bias 7, max 448) to v >= 0, ties to even, saturating.
@@ -130,30 +179,8 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v) {
     return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
-template <int RB>
-__device__ __forceinline__ void lowrank_mfma(f32x4 (&acc)[RB > 0 ? RB : 1], const Stage16<RB>& st,
-                                             const uint16_t* l1, int K, int rl, int k0) {
-    if constexpr (RB > 0) {
-        const bf16x8 a0 = as_bf16x8(st.xv0), a1 = as_bf16x8(st.xv1);
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            uint4 v0, v1;
-            if constexpr (kPrefetchL1<RB>) {
-                v0 = st.l1v[2 * b];
-                v1 = st.l1v[2 * b + 1];
-            } else {
-                const uint16_t* lr = l1 + (int64_t)(b * 16 + rl) * K + k0;
-                v0 = *reinterpret_cast<const uint4*>(lr);
-                v1 = *reinterpret_cast<const uint4*>(lr + 8);
-            }
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(v0), acc[b], 0, 0, 0);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(v1), acc[b], 0, 0, 0);
-        }
-    }
-}
-
-// Sum the 16 waves' partial low-rank products in a fixed tree order and store bf16 lora_act.
-// red holds 8 waves x RB x 256 floats.
+// Sum the waves' partial low-rank products in a fixed tree order and store bf16 lora_act.
+// red holds kQWaves / 2 x RB x 256 floats.
 template <int RB>
 __device__ __forceinline__ void lowrank_finish(f32x4 (&acc)[RB > 0 ? RB : 1], float* red,
                                                int64_t m0, int64_t M, uint16_t* lora) {
@@ -187,126 +214,139 @@ __device__ __forceinline__ void lowrank_finish(f32x4 (&acc)[RB > 0 ? RB : 1], fl
     }
 }
 
-// Quantize one (16 rows x 64 channels) group held by the wave and write its codes.
-template <int MODE>
-__device__ __forceinline__ void quantize_group(const float (&xh)[16], int64_t row, bool valid,
-                                               int g, int G, int K, int kc, float den,
-                                               const QuantArgs& p) {
-    const int quarter = kc >> 4;
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xh[i]));
+// Quantize and store the lane's 32 channels (half h of group g) of one row.
+template <int MODE, int RB>
+__device__ __forceinline__ void quantize_half(const Stage<RB>& st, const float* si, int64_t row,
+                                              bool row_ok, int g, int h, int G, int K,
+                                              const QuantArgs& p) {
+    Vals v;
+    smooth32<RB>(v, st, si);
     if constexpr (MODE != kNvfp4Nibbles) {
-        // INT4: the 64-channel group spans the four lanes of this row
-        a = wave_max_xor(a, 16);
-        a = wave_max_xor(a, 32);
+        float a = absmax32(v);
+        a = fmaxf(a, __shfl_xor(a, 16, 64));   // the group's other half
         const float s = a / 7.0f;
-        float q[16];
-        int4_codes(xh, s, q);
+        int4_codes32<RB>(v, s, st, si);
         if constexpr (MODE == kInt4Nibbles) {
-            uint32_t p0 = 0u, p1 = 0u;
+            uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const uint32_t nib = (uint32_t)(int)q[i] & 15u;
-                if (i < 8) p0 |= nib << (4 * i);
-                else p1 |= nib << (4 * (i - 8));
+                const uint32_t pair = ((uint32_t)(int)v.ev[i] & 15u) | (((uint32_t)(int)v.od[i] & 15u) << 4);
+                d[i >> 2] |= pair << (8 * (i & 3));
             }
-            if (valid) {
-                *reinterpret_cast<uint2*>((uint8_t*)p.codes + row * (K / 2) + (g * 64 + kc) / 2) =
-                    make_uint2(p0, p1);
-                if (quarter == 0) reinterpret_cast<float*>(p.scales)[row * G + g] = s;
+            if (row_ok) {
+                *reinterpret_cast<uint4*>((uint8_t*)p.codes + row * (K / 2) + g * 32 + h * 16) =
+                    make_uint4(d[0], d[1], d[2], d[3]);
+                if (h == 0) reinterpret_cast<float*>(p.scales)[row * G + g] = s;
             }
         } else {
-            // FP6 fields (sign << 5 | |q|) of channels 16 (quarter & 1) + i of MFMA lane
-            // L = row % 32 + 32 (quarter >> 1): bits 96 (quarter & 1) + 6 i of its six dwords
-            uint32_t d[3] = {0u, 0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int qi = (int)q[i];
-                const uint32_t f = (uint32_t)fabsf(q[i]) | (((uint32_t)qi >> 26) & 32u);
-                const int pos = 6 * i;
-                d[pos >> 5] |= f << (pos & 31);
-                if ((pos & 31) > 26) d[(pos >> 5) + 1] |= f >> (32 - (pos & 31));
-            }
-            const int r32 = (int)(row & 31), L = r32 + 32 * (quarter >> 1);
+            // fields 2i <- channel 2i, 2i+1 <- channel 2i+1; value q / 8 (exact)
+            const u32x6 f = cvt_fp6x32(v.ev, v.od, 8.0f);
+            const int r32 = (int)(row & 31), L = r32 + 32 * h;
             uint8_t* blk = (uint8_t*)p.codes + packed::act_block(row, g, G);
-            const bool odd = quarter & 1;
-            // even quarter: dwords 0-2 of the lane; odd quarter: dwords 3-5
-            *reinterpret_cast<uint2*>(blk + (odd ? packed::frag_dword(L, 4) : packed::frag_dword(L, 0))) =
-                odd ? make_uint2(d[1], d[2]) : make_uint2(d[0], d[1]);
-            *reinterpret_cast<uint32_t*>(blk + (odd ? packed::frag_dword(L, 3) : packed::frag_dword(L, 2))) =
-                odd ? d[0] : d[2];
-            if (quarter == 0) {
+            *reinterpret_cast<uint4*>(blk + packed::frag_dword(L, 0)) = make_uint4(f[0], f[1], f[2], f[3]);
+            *reinterpret_cast<uint2*>(blk + packed::frag_dword(L, 4)) = make_uint2(f[4], f[5]);
+            if (h == 0) {
                 const uint32_t hi = f32_to_bf16(s);
                 const uint32_t lo = f32_to_bf16(s - __uint_as_float(hi << 16));
                 *reinterpret_cast<uint32_t*>(blk + packed::kFrag + 4 * r32) = hi | (lo << 16);
-                if (valid && p.scales) reinterpret_cast<float*>(p.scales)[row * G + g] = s;
+                if (row_ok && p.scales) reinterpret_cast<float*>(p.scales)[row * G + g] = s;
             }
         }
     } else {
-        // NVFP4: this lane's 16 channels are one block
-        const uint32_t sb = e4m3_encode(a / den);
-        uint32_t p0 = 0u, p1 = 0u;
-        if (sb != 0u) {
-            const float dq = e4m3_decode(sb) * p.S;
+        // NVFP4: the lane's 32 channels are two blocks of 16 (channels 0-15: ev/od 0-7)
+        const float den = 6.0f * p.S;
+        uint32_t d[4] = {0u, 0u, 0u, 0u};
+        uint32_t sbs = 0u;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t c = e2m1_encode(xh[i] / dq);
-                if (i < 8) p0 |= c << (4 * i);
-                else p1 |= c << (4 * (i - 8));
+        for (int b = 0; b < 2; ++b) {
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 8 * b; i < 8 * b + 8; ++i) a = fmaxf(a, fmaxf(fabsf(v.ev[i]), fabsf(v.od[i])));
+            const uint32_t sb = e4m3_encode(a / den);
+            sbs |= sb << (8 * b);
+            if (sb != 0u) {
+                const float dq = e4m3_decode(sb) * p.S;
+#pragma unroll
+                for (int i = 8 * b; i < 8 * b + 8; ++i) {
+                    const uint32_t pair = e2m1_encode(v.ev[i] / dq) | (e2m1_encode(v.od[i] / dq) << 4);
+                    d[i >> 2] |= pair << (8 * (i & 3));
+                }
             }
         }
-        if (valid) {
-            const int k0 = g * 64 + kc;
-            reinterpret_cast<uint8_t*>(p.scales)[row * (K / 16) + k0 / 16] = (uint8_t)sb;
-            *reinterpret_cast<uint2*>((uint8_t*)p.codes + row * (K / 2) + k0 / 2) = make_uint2(p0, p1);
+        if (row_ok) {
+            const int k0 = g * 64 + h * 32;
+            uint8_t* sp = (uint8_t*)p.scales + row * (K / 16) + k0 / 16;
+            sp[0] = (uint8_t)sbs;
+            sp[1] = (uint8_t)(sbs >> 8);
+            *reinterpret_cast<uint4*>((uint8_t*)p.codes + row * (K / 2) + k0 / 2) =
+                make_uint4(d[0], d[1], d[2], d[3]);
         }
     }
 }
 
 template <int RB, int MODE>
 __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
-    extern __shared__ __align__(16) float qsm[];
-    const int K = p.K;
-    const int64_t M = p.M;
-    float* si_lds = qsm;                     // K floats
-    float* red = qsm + K;                    // 8 * RB * 256 floats
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t m0 = (int64_t)blockIdx.x * kRows;
-    const int rl = lane & 15, kc = (lane >> 4) * 16;
-    const int64_t row = m0 + rl;
-    const bool valid = row < M;
-    const uint16_t* x = (const uint16_t*)p.x;
-    const uint16_t* l1 = (const uint16_t*)p.l1;
-    const uint16_t* xr = x + (valid ? row : M - 1) * (int64_t)K;
-    const int G = K >> 6;
-    const int ng = G > wave ? (G - wave + kQWaves - 1) / kQWaves : 0;   // this wave's groups
     constexpr int NA = kAhead<RB>;
+    __shared__ __align__(16) float red[(kQWaves / 2) * (RB > 0 ? RB : 1) * 256];
+    __shared__ __align__(16) float si_lds[kQWaves][NA][kStep];
+    const int K = p.K, G = K >> 6;
+    const int64_t M = p.M;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t m0 = (int64_t)blockIdx.x * kRows;
+    const int rl = lane & 15, q4 = lane >> 4;   // row, quarter of the step
+    const int64_t row = m0 + rl;
+    const bool row_ok = row < M;
+    const uint16_t* xr = (const uint16_t*)p.x + (row_ok ? row : M - 1) * (int64_t)K;
+    const uint16_t* l1r = (const uint16_t*)p.l1 + (int64_t)rl * K;
+    const int nc = (G + 1) >> 1;                                       // steps over K
+    const int nsw = nc > wave ? (nc - wave + kQWaves - 1) / kQWaves : 0;  // this wave's steps
     f32x4 acc[RB > 0 ? RB : 1];
 #pragma unroll
     for (int b = 0; b < (RB > 0 ? RB : 1); ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    Stage16<RB> st[NA];
-#pragma unroll
-    for (int s = 0; s < NA; ++s)
-        if (s < ng) load_stage<RB>(st[s], xr, l1, K, rl, (wave + s * kQWaves) * 64 + kc);
-    for (int i = threadIdx.x * 4; i < K; i += kQThreads * 4)
-        *reinterpret_cast<float4*>(si_lds + i) = *reinterpret_cast<const float4*>(p.smooth_inv + i);
-    __syncthreads();
-    const float den = 6.0f * p.S;
-
-    for (int it0 = 0; it0 < ng; it0 += NA) {
+    for (int it0 = 0; it0 < nsw; it0 += NA) {
+        // loads of up to NA steps, unconditional (clamped) so the waits stay exact
+        uint2 siv[NA];
+        Stage<RB> st[NA];
 #pragma unroll
         for (int s = 0; s < NA; ++s) {
-            const int it = it0 + s;
-            if (it < ng) {
-                const int g = wave + it * kQWaves;
-                const int k0 = g * 64 + kc;
-                float xh[16];
-                smooth16<RB>(xh, st[s], si_lds + k0, valid);
-                quantize_group<MODE>(xh, row, valid, g, G, K, kc, den, p);
-                lowrank_mfma<RB>(acc, st[s], l1, K, rl, k0);
-                if (it + NA < ng) load_stage<RB>(st[s], xr, l1, K, rl, k0 + NA * kQWaves * 64);
+            const int c = wave + kQWaves * min(it0 + s, nsw - 1);
+            siv[s] = *reinterpret_cast<const uint2*>(p.smooth_inv + min(c * kStep + 2 * lane, K - 2));
+        }
+#pragma unroll
+        for (int s = 0; s < NA; ++s) {
+            const int c = wave + kQWaves * min(it0 + s, nsw - 1);
+            load_stage<RB>(st[s], xr, l1r, K, min(c * kStep + 32 * q4, K - 32));
+        }
+#pragma unroll
+        for (int s = 0; s < NA; ++s) *reinterpret_cast<uint2*>(&si_lds[wave][s][2 * lane]) = siv[s];
+#pragma unroll
+        for (int s = 0; s < NA; ++s) {
+            if (it0 + s < nsw) {
+                const int c = wave + kQWaves * (it0 + s);
+                const int g = 2 * c + (q4 >> 1), h = q4 & 1;
+                const bool g_ok = g < G;   // the last step of an odd group count is half full
+                if (!(row_ok && g_ok)) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) st[s].x[t] = make_uint4(0u, 0u, 0u, 0u);
+                }
+                const float* si = &si_lds[wave][s][32 * q4];
+                if (g_ok && (MODE == kInt4Packed || row_ok))
+                    quantize_half<MODE, RB>(st[s], si, row, row_ok, g, h, G, K, p);
+                if constexpr (RB > 0) {
+                    const int k0 = min(c * kStep + 32 * q4, K - 32);
+#pragma unroll
+                    for (int b = 0; b < RB; ++b)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            uint4 w;
+                            if constexpr (kPrefetchL1<RB>) w = st[s].l1[4 * b + t];
+                            else w = load_l1(l1r, K, b, k0, t);
+                            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(st[s].x[t]), as_bf16x8(w), acc[b], 0, 0, 0);
+                        }
+                }
             }
         }
     }
@@ -315,15 +355,8 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
 
 template <int RB, int MODE>
 void launch_mode(const QuantArgs& a, int64_t rows, hipStream_t st) {
-    const size_t lds = ((size_t)a.K + 8 * (size_t)RB * 256) * sizeof(float);
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)quant_act_kernel<RB, MODE>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kQuantMaxLds);
-        attr_set = true;
-    }
     hipLaunchKernelGGL((quant_act_kernel<RB, MODE>), dim3((unsigned)((rows + kRows - 1) / kRows)),
-                       dim3(kQThreads), lds, st, a);
+                       dim3(kQThreads), 0, st, a);
 }
 
 template <int RB>
@@ -340,10 +373,6 @@ void launch_rb(const QuantArgs& a, hipStream_t st) {
 }
 
 }  // namespace
-
-size_t quantize_act_lds_bytes(int K, int r) {
-    return ((size_t)K + 8 * (size_t)(r / 16) * 256) * sizeof(float);
-}
 
 void launch_quantize_act(const QuantArgs& a, hipStream_t st) {
     switch (a.r / 16) {
