@@ -10,12 +10,12 @@
 // rate and returns fp32, and v_mfma_scale_f32_32x32x64_f8f6f4 contracts exactly one group.
 // Per 32x32 output tile and group:
 //   R = mfma_fp6(A_g, W_g)               = D_g / 64, exact
-//   P = mfma_bf16(sa hi/lo, 64 sw hi/lo) = 64 sa[m] sw[n]  (relative error ~2^-16)
+//   P = mfma_bf16(sa, 64 sw as 3-term bf16 splits) = 64 sa[m] sw[n]  (to a few fp32 ulp)
 //   acc = fma(R, P, acc)                 the only VALU work per output and group
 // Both operands arrive in the layout of packed_layout.hpp (activations from
 // svdq_quantize_act_packed or svdq_pack_act, weights from svdq_prepack_weight), so a
-// pipeline stage is a plain copy: 25 KiB per (256x192 tile, group) moved global -> LDS by
-// the LDS-DMA path (global_load_lds_dwordx4), 6 stages deep, one barrier per group.
+// pipeline stage is a plain copy: 26 KiB per (256x192 tile, group) moved global -> LDS by
+// the LDS-DMA path (global_load_lds_dwordx4), double-buffered in halves of three groups.
 //
 // Tiling: 256x192 output tile per 512-thread workgroup, 8 waves as 4 x 2, each 64x96 =
 // 2 x 3 tiles of 32x32.  Workgroup ids are remapped so the workgroups an XCD runs at once
@@ -29,12 +29,12 @@ namespace {
 
 using namespace packed;
 
-constexpr int kThreads = 512, kStages = 6;
-constexpr int kStageBytes = kAStage + kBStage;   // 25600
-constexpr int kAChunks = kAStage / 1024;         // 13
+constexpr int kThreads = 512, kStages = 6, kHalf = kStages / 2;
+constexpr int kStageBytes = kAStage + kBStage;   // 26624
+constexpr int kAChunks = kAStage / 1024;         // 14
 constexpr int kBChunks = kBStage / 1024;         // 12
 static_assert(kAStage % 1024 == 0 && kBStage % 1024 == 0, "stages are whole 1 KiB chunks");
-static_assert(kAChunks + kBChunks == 25, "chunk assignment below assumes 25 chunks");
+static_assert(kAChunks + kBChunks == 26, "chunk assignment below assumes 26 chunks");
 constexpr int kSmemBytes = kStages * kStageBytes;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -46,29 +46,6 @@ template <int n>
 __device__ __forceinline__ void wait_vm() {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));
-}
-
-// wait_vm<n> for a wave-uniform n in [0, 16].
-__device__ __forceinline__ void wait_vm_dyn(int n) {
-    switch (n) {
-        case 0: wait_vm<0>(); break;
-        case 1: wait_vm<1>(); break;
-        case 2: wait_vm<2>(); break;
-        case 3: wait_vm<3>(); break;
-        case 4: wait_vm<4>(); break;
-        case 5: wait_vm<5>(); break;
-        case 6: wait_vm<6>(); break;
-        case 7: wait_vm<7>(); break;
-        case 8: wait_vm<8>(); break;
-        case 9: wait_vm<9>(); break;
-        case 10: wait_vm<10>(); break;
-        case 11: wait_vm<11>(); break;
-        case 12: wait_vm<12>(); break;
-        case 13: wait_vm<13>(); break;
-        case 14: wait_vm<14>(); break;
-        case 15: wait_vm<15>(); break;
-        default: wait_vm<16>(); break;
-    }
 }
 
 // Workgroup barrier without the memory fence __syncthreads() adds (that fence would wait
@@ -132,9 +109,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     const uint32_t lds0 = lds_offset(smem);
     const uint32_t voff = lane * 16;
 
-    // Stage chunks: 0-12 activations, 13-24 weights.  Wave w copies chunks w, w + 8 and
-    // w + 16; wave 0 also chunk 24.
-    const bool w0 = wave == 0;
+    // Stage chunks: 0-13 activations, 14-25 weights.  Wave w copies chunks w, w + 8 and
+    // w + 16; waves 0 and 1 also chunks 24 and 25.
     auto issue = [&](int h, int slot) {
         const uint8_t* ag = a_base + (int64_t)h * kAStage;
         const uint8_t* bg = b_base + (int64_t)h * kBStage;
@@ -143,11 +119,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         if (wave + 8 < kAChunks) dma_chunk(ag + (wave + 8) * 1024, voff, dst + (wave + 8) * 1024);
         else dma_chunk(bg + (wave + 8 - kAChunks) * 1024, voff, dst + (wave + 8) * 1024);
         dma_chunk(bg + (wave + 16 - kAChunks) * 1024, voff, dst + (wave + 16) * 1024);
-        if (w0) dma_chunk(bg + (24 - kAChunks) * 1024, voff, dst + 24 * 1024);
+        if (wave < 2) dma_chunk(bg + (wave + 24 - kAChunks) * 1024, voff, dst + (wave + 24) * 1024);
     };
 
-    const int npro = min(G, kStages - 1);
-    for (int h = 0; h < npro; ++h) issue(h, h);
+    // Double buffer of kHalf groups: one barrier per kHalf groups, after which the next
+    // kHalf groups' copies are issued into the half that was just consumed.  (A ring with a
+    // barrier every group serializes the copies with the arithmetic on gfx950.)
+    const int fr = lane & 31, fh = lane >> 5;
+    // byte selectors of v_perm_b32 (bytes 0-3: the l word, 4-7: the h | m << 16 word)
+    const uint32_t psel0 = fh ? 0x07060100u : 0x05040504u;
+    const uint32_t psel1 = fh ? 0x01000706u : 0x05040706u;
+
+    // The low-rank up-projection goes first: acc = lora_act . l2^T.  Its operand loads
+    // (and the bias) are issued ahead of the first copies, so their latency hides behind
+    // the wait for the first half instead of standing in the epilogue.
+    const uint16_t* lora = (const uint16_t*)p.lora;
+    const uint16_t* l2 = (const uint16_t*)p.l2;
+    const int r = p.r;
+    int64_t mrow[2];
+    int ncol[3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) mrow[i] = min(m0 + wm * 64 + i * 32 + fr, M - 1);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) ncol[j] = min(n0 + wn * 96 + j * 32 + fr, N - 1);
+    uint4 la[2][2], lb[3][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        if (16 * c < r) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) la[i][c] = *reinterpret_cast<const uint4*>(lora + mrow[i] * r + 16 * c + 8 * fh);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) lb[j][c] = *reinterpret_cast<const uint4*>(l2 + (int64_t)ncol[j] * r + 16 * c + 8 * fh);
+        }
+    const uint16_t* bias = (const uint16_t*)p.bias;
+    float bv[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int col = n0 + wn * 96 + j * 32 + fr;
+        bv[j] = (bias && col < N) ? bf16_to_f32(bias[col]) : 0.0f;
+    }
+
+    for (int h = 0; h < min(G, kHalf); ++h) issue(h, h);
 
     f32x16 acc[2][3];
 #pragma unroll
@@ -156,83 +168,105 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         for (int j = 0; j < 3; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    const int fr = lane & 31;
-    int slot = 0, islot = kStages - 1;
-    for (int g = 0; g < G; ++g) {
-        // group g has landed once at most the DMAs of groups g+1 .. g+kStages-2 are pending
-        if (g + kStages - 2 < G) {
-            if (w0) wait_vm<4 * (kStages - 2)>();
-            else wait_vm<3 * (kStages - 2)>();
-        } else {
-            wait_vm_dyn((w0 ? 4 : 3) * (G - 1 - g));
+    wait_vm<0>();   // the first half and the operands above have landed
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        if (16 * c < r) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(la[i][c]), as_bf16x8(lb[j][c]),
+                                                                        acc[i][j], 0, 0, 0);
         }
-        barrier();   // every wave's copy of group g is visible; stage of group g-1 is free
-        if (g + kStages - 1 < G) issue(g + kStages - 1, islot);
-        islot = islot + 1 == kStages ? 0 : islot + 1;
+    for (int kk = 32; kk < r; kk += 16) {   // ranks beyond 32
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint4 va = *reinterpret_cast<const uint4*>(lora + mrow[i] * r + kk + 8 * fh);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const uint4 vb = *reinterpret_cast<const uint4*>(l2 + (int64_t)ncol[j] * r + kk + 8 * fh);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(vb), acc[i][j], 0, 0, 0);
+            }
+        }
+    }
 
-        const uint8_t* S = smem + slot * kStageBytes;
-        slot = slot + 1 == kStages ? 0 : slot + 1;
-        i32x8 aop[2];
-        bf16x4 apop[2];
+    // The operands of this wave for one group: two activation fragments and their scale
+    // operands, three weight fragments and theirs.  Within a half, the next group's
+    // operands are read from LDS while the current group computes.
+    struct Frags {
+        i32x8 a[2];
+        bf16x4 ap[2];
+        i32x8 w[3];
+        bf16x4 wp[3];
+    };
+    auto load_frags = [&](const uint8_t* S, Frags& f) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const uint8_t* Ab = S + (2 * wm + i) * kABlock;
             const uint4 v0 = *reinterpret_cast<const uint4*>(Ab + lane * 16);
             const uint2 v1 = *reinterpret_cast<const uint2*>(Ab + 1024 + lane * 8);
-            const uint32_t x = *reinterpret_cast<const uint32_t*>(Ab + kFrag + fr * 4);
-            aop[i].s0123 = i32x4{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w};
-            aop[i].s45 = (__attribute__((ext_vector_type(2))) int){(int)v1.x, (int)v1.y};
-            apop[i] = __builtin_bit_cast(bf16x4, make_uint2(x, x & 0xFFFFu));
+            const uint2 x = *reinterpret_cast<const uint2*>(Ab + kFrag + fr * 8);
+            f.a[i].s0123 = i32x4{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w};
+            f.a[i].s45 = (__attribute__((ext_vector_type(2))) int){(int)v1.x, (int)v1.y};
+            // (h | m << 16, l) -> lanes 0-31 (h, h, m, h), lanes 32-63 (l, m, m, l)
+            f.ap[i] = __builtin_bit_cast(bf16x4, make_uint2(__builtin_amdgcn_perm(x.x, x.y, psel0),
+                                                            __builtin_amdgcn_perm(x.x, x.y, psel1)));
         }
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const uint8_t* Bb = S + kAStage + (3 * wn + j) * kBBlock;
             const uint4 w0v = *reinterpret_cast<const uint4*>(Bb + lane * 16);
             const uint2 w1v = *reinterpret_cast<const uint2*>(Bb + 1024 + lane * 8);
-            const uint2 wp = *reinterpret_cast<const uint2*>(Bb + kFrag + lane * 8);
-            i32x8 wop;
-            wop.s0123 = i32x4{(int)w0v.x, (int)w0v.y, (int)w0v.z, (int)w0v.w};
-            wop.s45 = (__attribute__((ext_vector_type(2))) int){(int)w1v.x, (int)w1v.y};
-            const bf16x4 wpop = __builtin_bit_cast(bf16x4, wp);
+            f.w[j].s0123 = i32x4{(int)w0v.x, (int)w0v.y, (int)w0v.z, (int)w0v.w};
+            f.w[j].s45 = (__attribute__((ext_vector_type(2))) int){(int)w1v.x, (int)w1v.y};
+            f.wp[j] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(Bb + kFrag + lane * 8));
+        }
+    };
+    auto compute = [&](const Frags& f) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const f32x16 r = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    aop[i], wop, f32x16{}, 2, 2, 0, 127, 0, 127);
-                const f32x16 pp = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(apop[i], wpop, f32x16{}, 0, 0, 0);
+                    f.a[i], f.w[j], f32x16{}, 2, 2, 0, 127, 0, 127);
+                const f32x16 pp = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(f.ap[i], f.wp[j], f32x16{}, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(r[e], pp[e], acc[i][j][e]);
             }
+    };
+
+    static_assert(kHalf == 3, "the unrolled half below is written for three groups");
+    const int g_full = G - G % kHalf;
+    for (int g0 = 0; g0 < g_full; g0 += kHalf) {
+        wait_vm<0>();   // this wave's copies of groups g0 .. g0+2 have landed
+        barrier();      // every wave's have; the other half is no longer read
+        const int h1 = min(G, g0 + 2 * kHalf);
+        for (int h = g0 + kHalf; h < h1; ++h) issue(h, h % kStages);
+
+        const uint8_t* S0 = smem + (g0 % kStages) * kStageBytes;
+        Frags f0, f1;
+        load_frags(S0, f0);
+        load_frags(S0 + kStageBytes, f1);
+        compute(f0);
+        __builtin_amdgcn_sched_barrier(0);   // keep groups apart (register pressure)
+        load_frags(S0 + 2 * kStageBytes, f0);
+        compute(f1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(f0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (g_full < G) {   // the last G % 3 groups
+        wait_vm<0>();
+        barrier();
+        for (int g = g_full; g < G; ++g) {
+            Frags f;
+            load_frags(smem + (g % kStages) * kStageBytes, f);
+            compute(f);
         }
     }
 
-    // ---- epilogue: low-rank up-projection on the MFMA, bias, GELU, store
-    const uint16_t* lora = (const uint16_t*)p.lora;
-    const uint16_t* l2 = (const uint16_t*)p.l2;
-    const int r = p.r, fh = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        int64_t mrow = m0 + wm * 64 + i * 32 + fr;
-        if (mrow >= M) mrow = M - 1;
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            int ncol = n0 + wn * 96 + j * 32 + fr;
-            if (ncol >= N) ncol = N - 1;
-            for (int kk = 0; kk < r; kk += 16) {
-                const uint4 va = *reinterpret_cast<const uint4*>(lora + mrow * r + kk + 8 * fh);
-                const uint4 vb = *reinterpret_cast<const uint4*>(l2 + (int64_t)ncol * r + kk + 8 * fh);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(vb),
-                                                                    acc[i][j], 0, 0, 0);
-            }
-        }
-    }
-    const uint16_t* bias = (const uint16_t*)p.bias;
-    float bv[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int col = n0 + wn * 96 + j * 32 + fr;
-        bv[j] = (bias && col < N) ? bf16_to_f32(bias[col]) : 0.0f;
-    }
+    // ---- epilogue: bias, GELU, store
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -312,12 +346,6 @@ __device__ __forceinline__ void nibbles_to_fp6(const uint8_t* src, uint32_t (&w)
     }
 }
 
-// hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo) {
-    hi = f32_to_bf16(x);
-    lo = f32_to_bf16(x - __uint_as_float(hi << 16));
-}
-
 // ---------------------------------------------------------------- weight prepack
 // One 64-thread block per (32-column block, group); lane L covers column L % 32 and
 // channel half L / 32 of the group: the B-operand lane of the FP6 MFMA.
@@ -335,9 +363,8 @@ __global__ __launch_bounds__(64) void prepack_wgt_kernel(int N, int K, int ncb,
     uint8_t* blk = out + wgt_block(n, g, G);
     *reinterpret_cast<uint4*>(blk + frag_dword(L, 0)) = make_uint4(w[0], w[1], w[2], w[3]);
     *reinterpret_cast<uint2*>(blk + frag_dword(L, 4)) = make_uint2(w[4], w[5]);
-    uint32_t hi = 0u, lo = 0u;
-    if (half == 0 && valid) split_hi_lo(wscales[(int64_t)n * G + g] * 64.0f, hi, lo);
-    *reinterpret_cast<uint2*>(blk + kFrag + 8 * L) = make_uint2(hi | (hi << 16), lo);
+    const float w64 = valid ? wscales[(int64_t)n * G + g] * 64.0f : 0.0f;
+    *reinterpret_cast<uint2*>(blk + kFrag + 8 * L) = wgt_scale_operand(w64, L);
 }
 
 // ---------------------------------------------------------------- activation pack
@@ -358,11 +385,8 @@ __global__ __launch_bounds__(64) void pack_act_kernel(int64_t M, int K, int64_t 
     uint8_t* blk = out + act_block(m, g, G);
     *reinterpret_cast<uint4*>(blk + frag_dword(L, 0)) = make_uint4(w[0], w[1], w[2], w[3]);
     *reinterpret_cast<uint2*>(blk + frag_dword(L, 4)) = make_uint2(w[4], w[5]);
-    if (half == 0) {
-        uint32_t hi = 0u, lo = 0u;
-        if (valid) split_hi_lo(ascales[m * G + g], hi, lo);
-        *reinterpret_cast<uint32_t*>(blk + kFrag + 4 * r) = hi | (lo << 16);
-    }
+    if (half == 0)
+        *reinterpret_cast<uint2*>(blk + kFrag + 8 * r) = act_scale_pair(valid ? ascales[m * G + g] : 0.0f);
 }
 
 }  // namespace

@@ -9,20 +9,24 @@
 // 16-byte and one 8-byte access, both conflict-free in LDS:
 //   bytes [0, 1024)     dwords 0-3 of lane L at 16 L
 //   bytes [1024, 1536)  dwords 4-5 of lane L at 1024 + 8 L
-// followed by the operand of the bf16 scale MFMA (v_mfma_f32_32x32x8_bf16), which forms the
-// outer product sa[m] * 64 sw[n] from bf16 hi/lo splits (hi = bf16(s), lo = bf16(s - hi)):
-//   activations: 32 words (sa_hi | sa_lo << 16), one per row               (128 bytes)
-//   weights:     64 lane pairs; lanes 0-31 (w_hi | w_hi << 16, w_lo) for column L with
-//                w = 64 sw, lanes 32-63 zero                               (512 bytes)
-// so that sum_k A[m,k] B[k,n] = sa_hi w_hi + sa_lo w_hi + sa_hi w_lo.
+// followed by the operands of the bf16 scale MFMA (v_mfma_f32_32x32x8_bf16), which forms
+// the outer product sa[m] * w[n], w = 64 sw, from three-term bf16 splits
+// (h = bf16(s), m = bf16(s - h), l = bf16(s - h - m); h + m + l = s to ~2^-24):
+//   activations: per row (h | m << 16, l)                                   (256 bytes)
+//   weights:     per MFMA lane, lanes 0-31 (column L) (h | m << 16, h | l << 16),
+//                lanes 32-63 (column L - 32) (h | m << 16, l | m << 16)   (512 bytes)
+// With the activation lanes arranged as (ha, ha, ma, ha | la, ma, ma, la) the eight
+// products sum to (ha + ma + la)(hw + mw + lw) - la lw: the fp32 product to a few ulp.
 //
-// Activation buffer:  [ceil(M / 256)][G][8 row blocks][1664 bytes]
+// Activation buffer:  [ceil(M / 256)][G][8 row blocks][1792 bytes]
 // Weight buffer:      [ceil(N / 192)][G][6 column blocks][2048 bytes]
-// One (256-row block, group) is 13 KiB and one (192-column block, group) 12 KiB, each
+// One (256-row block, group) is 14 KiB and one (192-column block, group) 12 KiB, each
 // contiguous, which is what one GEMM pipeline stage copies.
 #pragma once
 
 #include <stdint.h>
+
+#include "common.hpp"
 
 namespace svdq {
 namespace packed {
@@ -31,9 +35,9 @@ constexpr int kBM = 256, kBN = 192;      // GEMM output tile per workgroup
 constexpr int kRB = kBM / 32;            // row blocks per tile
 constexpr int kCB = kBN / 32;            // column blocks per tile
 constexpr int kFrag = 1536;              // FP6 fragment bytes
-constexpr int kABlock = kFrag + 128;     // activation block: fragment + 32 scale words
+constexpr int kABlock = kFrag + 256;     // activation block: fragment + 32 scale pairs
 constexpr int kBBlock = kFrag + 512;     // weight block: fragment + 64 scale pairs
-constexpr int kAStage = kRB * kABlock;   // 13312
+constexpr int kAStage = kRB * kABlock;   // 14336
 constexpr int kBStage = kCB * kBBlock;   // 12288
 
 __host__ __device__ inline int64_t act_bytes(int64_t M, int K) {
@@ -54,6 +58,29 @@ __host__ __device__ inline int64_t wgt_block(int n, int g, int G) {
 // Byte offset, inside a block, of fragment dword d (0..5) of lane L.
 __host__ __device__ inline int frag_dword(int L, int d) {
     return d < 4 ? 16 * L + 4 * d : 1024 + 8 * L + 4 * (d - 4);
+}
+
+// Three-term bf16 split of s: h = bf16(s), m = bf16(s - h), l = bf16(s - h - m); both
+// subtractions are exact in fp32.
+__device__ __forceinline__ void split3(float s, uint32_t& h, uint32_t& m, uint32_t& l) {
+    h = f32_to_bf16(s);
+    const float r1 = s - __uint_as_float(h << 16);
+    m = f32_to_bf16(r1);
+    l = f32_to_bf16(r1 - __uint_as_float(m << 16));
+}
+
+// The activation scale pair of one row: (h | m << 16, l).
+__device__ __forceinline__ uint2 act_scale_pair(float s) {
+    uint32_t h, m, l;
+    split3(s, h, m, l);
+    return make_uint2(h | (m << 16), l);
+}
+
+// The weight scale operand of MFMA lane L for w = 64 sw of its column.
+__device__ __forceinline__ uint2 wgt_scale_operand(float w, int L) {
+    uint32_t h, m, l;
+    split3(w, h, m, l);
+    return L < 32 ? make_uint2(h | (m << 16), h | (l << 16)) : make_uint2(h | (m << 16), l | (m << 16));
 }
 
 }  // namespace packed

@@ -246,9 +246,7 @@ __device__ __forceinline__ void quantize_half(const Stage<RB>& st, const float* 
             *reinterpret_cast<uint4*>(blk + packed::frag_dword(L, 0)) = make_uint4(f[0], f[1], f[2], f[3]);
             *reinterpret_cast<uint2*>(blk + packed::frag_dword(L, 4)) = make_uint2(f[4], f[5]);
             if (h == 0) {
-                const uint32_t hi = f32_to_bf16(s);
-                const uint32_t lo = f32_to_bf16(s - __uint_as_float(hi << 16));
-                *reinterpret_cast<uint32_t*>(blk + packed::kFrag + 4 * r32) = hi | (lo << 16);
+                *reinterpret_cast<uint2*>(blk + packed::kFrag + 8 * r32) = packed::act_scale_pair(s);
                 if (row_ok && p.scales) reinterpret_cast<float*>(p.scales)[row * G + g] = s;
             }
         }

@@ -140,11 +140,11 @@ def _fp6_fields(dw):
 
 def decode_act_packed(buf, M, K):
     """Host-side reader of the packed activation layout (test infrastructure): returns the
-    int codes [Mp, K], the scale words (hi | lo << 16) [Mp, G] and a flag that every field
-    is canonical (no negative zero, magnitude <= 8)."""
+    int codes [Mp, K], the scale pairs (h | m << 16, l) [Mp, G, 2] and a flag that every
+    field is canonical (no negative zero, magnitude <= 8)."""
     G = K // 64
     mb = (M + 255) // 256
-    b = np.ascontiguousarray(np.asarray(buf, np.uint8)).reshape(mb, G, 8, 1664)
+    b = np.ascontiguousarray(np.asarray(buf, np.uint8)).reshape(mb, G, 8, 1792)
     p0 = np.ascontiguousarray(b[..., :1024]).view(np.uint32).reshape(mb, G, 8, 64, 4)
     p1 = np.ascontiguousarray(b[..., 1024:1536]).view(np.uint32).reshape(mb, G, 8, 64, 2)
     f = _fp6_fields(np.concatenate([p0, p1], axis=-1))          # mb, G, rb, lane, j
@@ -152,19 +152,22 @@ def decode_act_packed(buf, M, K):
     canonical = bool(np.all(mag <= 8) and not np.any((mag == 0) & (neg == 1)))
     q = np.where(neg == 1, -mag, mag).reshape(mb, G, 8, 2, 32, 32)  # lane = r + 32 h
     codes = q.transpose(0, 2, 4, 1, 3, 5).reshape(mb * 256, K)
-    words = np.ascontiguousarray(b[..., 1536:]).view(np.uint32).reshape(mb, G, 8, 32)
-    words = words.transpose(0, 2, 3, 1).reshape(mb * 256, G)
+    words = np.ascontiguousarray(b[..., 1536:]).view(np.uint32).reshape(mb, G, 8, 32, 2)
+    words = words.transpose(0, 2, 3, 1, 4).reshape(mb * 256, G, 2)
     return codes, words, canonical
 
 
 def split_words(scales):
-    """(hi | lo << 16) with hi = bf16(s), lo = bf16(s - hi), as the packed layout stores."""
+    """The scale pair the packed layout stores per (row, group): (h | m << 16, l) with
+    h = bf16(s), m = bf16(s - h), l = bf16(s - h - m)."""
     import synth
     s = np.asarray(scales, np.float32)
-    hi = synth.f32_to_bf16_bits(s).astype(np.uint32)
-    rest = (s - (hi << 16).view(np.float32)).astype(np.float32)
-    lo = synth.f32_to_bf16_bits(rest).astype(np.uint32)
-    return hi | (lo << 16)
+    h = synth.f32_to_bf16_bits(s).astype(np.uint32)
+    r1 = (s - (h << 16).view(np.float32)).astype(np.float32)
+    m = synth.f32_to_bf16_bits(r1).astype(np.uint32)
+    r2 = (r1 - (m << 16).view(np.float32)).astype(np.float32)
+    l = synth.f32_to_bf16_bits(r2).astype(np.uint32)
+    return np.stack([h | (m << 16), l], axis=-1)
 
 
 def awq(x_bf16, q, sc, z, bias=None, out_bf16=False):

@@ -180,13 +180,13 @@ def test_attn_projection_packed(workload_cache):
             e = gu.rel_fro(y[mi, ni], ref)
             print(f"attn packed gemm rel_fro={e:.3e}")
             assert e <= 1e-3
-    # end to end: GPU chain vs oracle chain from the same X
-    ye = gu.host(gu.gemm_packed(buf, wp, M, K, N, gl, L["l2"], L["bias"], out_bf16=True))
+    # end to end: GPU chain vs oracle chain from the same X (fp32 output: bf16 rounding
+    # alone is ~1e-3 relative and is checked element-wise above)
+    ye = gu.host(gu.gemm_packed(buf, wp, M, K, N, gl, L["l2"], L["bias"]))
     ref = oracle.gemm_w4a4_int4_at(mi, ni, oc, os_, L["wcodes"], L["wscales"], ol, L["l2"],
                                    L["bias"])
-    got = (ye[mi, ni].astype(np.uint32) << 16).view(np.float32)
-    e2e = gu.rel_fro(got, ref)
-    print(f"attn packed end-to-end (bf16 out) rel_fro={e2e:.3e}")
+    e2e = gu.rel_fro(ye[mi, ni], ref)
+    print(f"attn packed end-to-end rel_fro={e2e:.3e}")
     assert e2e <= 1e-3
 
 
