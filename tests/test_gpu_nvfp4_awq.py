@@ -57,7 +57,14 @@ def test_gemm_nvfp4_shapes(M, N, K, r, bias, act):
     gu.assert_bf16_close(yb, ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (2, 130, 3072), (5, 33, 512), (9, 100, 256)])
+# M <= 4 with K a multiple of 512 up to 4096 runs the MFMA kernel, everything else the
+# reference kernel; N not a multiple of 16 leaves a partial column tile; N = 25000 at
+# K = 3072 needs more workgroups than fit in LDS at once (several columns runs per CU)
+@pytest.mark.parametrize("M,N,K", [
+    (1, 64, 64), (2, 130, 3072), (5, 33, 512), (9, 100, 256), (3, 70, 768), (4, 96, 1024),
+    (2, 64, 1536), (1, 40, 2048), (4, 50, 4096), (6, 50, 4096), (2, 32, 1152), (2, 48, 4160),
+    (13, 200, 3072), (1, 25000, 3072), (2, 1000, 512),
+])
 def test_awq_shapes(M, N, K):
     rng = np.random.default_rng(600 + M + N + K)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
@@ -71,3 +78,26 @@ def test_awq_shapes(M, N, K):
         assert gu.rel_fro(y, ref) <= 1e-5
         yb = gu.host(gu.awq(x, q, sc, z, bias, out_bf16=True))
         gu.assert_bf16_close(yb, ref)
+
+
+def test_awq_unaligned_scales():
+    """Scales and zeros at 2-byte (not 16-byte) aligned addresses are accepted (they take
+    the reference kernel); results within the same bound as aligned ones."""
+    M, N, K = 2, 70, 3072
+    rng = np.random.default_rng(611)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    q, sc, z = oracle.awq_quant_weight(w)
+    x = synth.random_bf16(rng, (M, K), 1.0)
+    ref = oracle.awq_gemv(x, q, sc, z, None)
+
+    def shifted(a):
+        buf = torch.zeros(a.size + 1, dtype=torch.int16, device="cuda:0")
+        buf[1:] = gu.dev(a).reshape(-1)
+        return buf[1:].view(a.shape)
+
+    out = gu.empty((M, N), np.float32)
+    gu.bd.awq_gemm_w4a16(M, K, N, 64, gu.dev(x), gu.dev(q), shifted(sc), shifted(z), None,
+                         gu.bd.SVDQ_DT_F32, out)
+    y = gu.host(out)
+    assert gu.rel_fro(y, ref) <= 1e-5
+    assert gu.rel_fro(gu.host(gu.awq(x, q, sc, z, None)), ref) <= 1e-5
