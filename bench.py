@@ -6,15 +6,21 @@ GEMM (per-group dequantization, low-rank up-projection, bias), for the DiT atten
 projection at 1024x1024 image scale: M = 4096 tokens, K = N = 3072, rank 32, INT4 groups
 of 64, bf16 bias, bf16 output.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline] [--only-main]
+    python bench.py --copy-calibration      # plain 256 MiB device copies (counter calibration)
 
 Prints one JSON line.  `value` is TOPS of the linear, counting 2MNK + 2MNr + 2MKr
 operations per step (the low-rank branch's flops included, the dense bf16 work the method
 avoids not counted), with every input already in HBM.  Inputs rotate through enough copies
 (> 256 MB) that each step reads activations and weights from HBM, not from the MI355X's
-256 MB last-level cache.
+256 MB last-level cache.  Unless --only-main, the line also carries the secondary paths:
+the AWQ W4A16 GEMV of the adaLN modulation (M=2, K=3072, N=18432; GB/s against HBM) and the
+NVFP4 fused-QKV linear (M=4096, K=3072, N=9216, rank 32; TOPS against the bf16 and FP4
+peaks).  `roofline.traffic` comes from the HBM byte counters recorded for the GEMM kernel
+(profiles/), and is null when the kernel's sources changed since they were taken.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,7 +32,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0
+FP4_PEAK_TFLOPS = 10100.0
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+GEMM_SOURCES = ["bit_diffusion_amd/csrc/gemm_int4_fp6.hip", "bit_diffusion_amd/csrc/packed_layout.hpp"]
+TRAFFIC_FILE = "profiles/traffic_gemm_w4a4_packed_attn_4096x3072x3072.txt"
 
 M, K, N, R = 4096, 3072, 3072, 32
 WORKLOAD = "attn_4096x3072x3072_r32"
@@ -40,9 +50,143 @@ def parse():
     ap.add_argument("--copies", type=int, default=10,
                     help="rotating input sets (each ~30 MB) to defeat the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512,
+    ap.add_argument("--cpu-rows", type=int, default=1536,
                     help="token rows of the workload the CPU oracle baseline runs")
+    ap.add_argument("--only-main", action="store_true",
+                    help="time only the W4A4 linear (no AWQ / NVFP4 legs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run plain 256 MiB device copies only (for the byte-counter scale)")
     return ap.parse_args()
+
+
+def sources_hash(paths):
+    h = hashlib.sha256()
+    for pth in paths:
+        with open(os.path.join(ROOT, pth), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per GEMM launch from the recorded counter runs, if they were taken on the
+    current GEMM sources (key: value lines; see the file for the commands)."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256_16") != sources_hash(GEMM_SOURCES):
+        return None
+    try:
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """Plain device-to-device copies of 256 MiB: FETCH_SIZE / WRITE_SIZE of these dispatches
+    against the known 268,435,456 bytes each way give the counters' byte scale."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "copies": 10}), flush=True)
+
+
+def time_launches(fn, n, stream):
+    """Mean per-call time (ms) of n calls fn(i) on `stream`, events on that stream."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def awq_leg(steps, sp, stream):
+    """AWQ W4A16 GEMV of the modulation layers: M=2, K=3072, N=18432, 14 rotating weight
+    copies (> 400 MB, so every call streams its weights from HBM)."""
+    import torch
+    import synth
+    import bit_diffusion_amd as bd
+    Ma, Ka, Na, copies = 2, 3072, 18432, 14
+    rng = np.random.default_rng(11)
+    dev = "cuda:0"
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    qs = [torch.from_numpy(synth.random_packed_nibbles(rng, Na, Ka)).to(dev) for _ in range(copies)]
+    sc = [t16(synth.random_bf16(rng, (Na, Ka // 64), 0.01)) for _ in range(copies)]
+    zs = [t16(synth.f32_to_bf16_bits(rng.integers(0, 16, (Na, Ka // 64)).astype(np.float32)))
+          for _ in range(copies)]
+    x = t16(synth.random_bf16(rng, (Ma, Ka), 1.0))
+    b = t16(synth.random_bf16(rng, (Na,), 0.1))
+    out = torch.empty((Ma, Na), dtype=torch.float32, device=dev)
+
+    def go(i):
+        k = i % copies
+        bd.awq_gemm_w4a16(Ma, Ka, Na, 64, x, qs[k], sc[k], zs[k], b, bd.SVDQ_DT_F32, out, sp)
+
+    for i in range(copies):
+        go(i)
+    torch.cuda.synchronize()
+    ms = time_launches(go, max(steps, copies), stream)
+    nbytes = Na * Ka // 2 + 2 * Na * (Ka // 64) * 2 + Ma * Ka * 2 + Na * 2 + Ma * Na * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "awq_modulation_2x3072x18432", "us_per_call": round(ms * 1e3, 3),
+            "bytes": nbytes, "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def nvfp4_leg(steps, sp, stream):
+    """NVFP4 fused-QKV linear: activation kernel + GEMM, M=4096, K=3072, N=9216, rank 32."""
+    import torch
+    import synth
+    import bit_diffusion_amd as bd
+    Mn, Kn, Nn, Rn = 4096, 3072, 9216, 32
+    rng = np.random.default_rng(12)
+    dev = "cuda:0"
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    cfg = bd.LayerCfg.make(Kn, Nn, Rn, "nvfp4")
+    x = t16(synth.random_bf16(rng, (Mn, Kn), 1.0))
+    si = torch.ones(Kn, dtype=torch.float32, device=dev)
+    l1 = t16(synth.random_bf16(rng, (Rn, Kn), 0.02))
+    l2 = t16(synth.random_bf16(rng, (Nn, Rn), 0.02))
+    wc = torch.from_numpy(synth.random_packed_nibbles(rng, Nn, Kn)).to(dev)
+    ws = torch.from_numpy(rng.integers(0x30, 0x40, (Nn, Kn // 16)).astype(np.uint8)).to(dev)
+    bias = t16(synth.random_bf16(rng, (Nn,), 0.02))
+    ac = torch.empty((Mn, Kn // 2), dtype=torch.uint8, device=dev)
+    asb = torch.empty((Mn, Kn // 16), dtype=torch.uint8, device=dev)
+    lora = torch.empty((Mn, Rn), dtype=torch.int16, device=dev)
+    out = torch.empty((Mn, Nn), dtype=torch.int16, device=dev)
+    Sa, Sw = 0.002, 0.0005
+
+    def go(i):
+        bd.svdq_quantize_act(cfg, Mn, x, si, l1, Sa, ac, asb, lora, sp)
+        bd.svdq_gemm_w4a4(cfg, Mn, ac, asb, Sa, wc, ws, Sw, lora, l2, bias, bd.SVDQ_ACT_NONE,
+                          bd.SVDQ_DT_BF16, out, sp)
+
+    go(0)
+    torch.cuda.synchronize()
+    n = max(3, steps // 5)
+    ms = time_launches(go, n, stream)
+    ops = 2.0 * Mn * Nn * Kn + 2.0 * Mn * Nn * Rn + 2.0 * Mn * Kn * Rn
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"workload": "nvfp4_qkv_4096x3072x9216_r32", "ms_per_linear": round(ms, 4),
+            "TOPS": round(tops, 2), "bf16_peak_frac": round(tops / BF16_PEAK_TFLOPS, 4),
+            "fp4_peak_frac": round(tops / FP4_PEAK_TFLOPS, 4)}
 
 
 def make_inputs(copies):
@@ -134,6 +278,9 @@ def main():
     import torch
     import bit_diffusion_amd as bd
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     assert bd.svdq_check_device(0) == bd.SVDQ_OK, bd.svdq_last_error()
     si, sets, _ = make_inputs(args.copies)
     cfg = bd.LayerCfg.make(K, N, R)
@@ -187,6 +334,7 @@ def main():
     quant_bytes = (M * K * 2 + K * 4 + R * K * 2 + M * K * 3 // 4 + M * (K // 64) * 8
                    + M * R * 2)
     quant_gbs = quant_bytes / (t_q.mean() * 1e-3) / 1e9
+    traffic = recorded_traffic()
 
     out = {
         "metric": "W4A4+low-rank r32 linear TOPS @4096x3072x3072; % of int8 MFMA peak",
@@ -206,7 +354,7 @@ def main():
                    round(100 * value / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": None, "kernel": "svdq_gemm_w4a4_packed (int4 as FP6 on the MFMA)",
+                     "traffic": traffic, "kernel": "svdq_gemm_w4a4_packed (int4 as FP6 on the MFMA)",
                      "ms_per_launch": round(float(t_g.mean()), 5)},
         "kernels": {
             "quantize_act_ms": round(float(t_q.mean()), 5),
@@ -216,6 +364,9 @@ def main():
             "gemm_TOPS": round(gemm_tops, 2),
         },
     }
+    if not args.only_main:
+        out["awq"] = awq_leg(args.steps, sp, stream)
+        out["nvfp4"] = nvfp4_leg(args.steps, sp, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     print(json.dumps(out), flush=True)
