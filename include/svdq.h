@@ -151,11 +151,13 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
  * kernel hands the GEMM its 4-bit operands in the layout the matrix unit consumes).
  * Both operands are stored as exact FP6 (E2M3) values q/8 of the int4 codes in the lane
  * order of the gfx950 32x32x64 FP6 MFMA, 32 rows (or columns) x 64 channels per fragment,
- * each followed by the group scales as bf16 hi/lo pairs (hi = bf16(s), lo = bf16(s - hi)).
- * Activations take 6 bits per code plus 4 bytes per (row, group) and are padded to a
- * multiple of 256 rows; weights take 6 bits per code plus 16 bytes per (column, group) and
- * are padded to a multiple of 192 columns.  The buffers are opaque; sizes come from the
- * *_bytes queries.  All buffers are device memory, 16-byte aligned, owned by the caller.
+ * each followed by the group scales as three-term bf16 splits (h = bf16(s), m = bf16(s - h),
+ * l = bf16(s - h - m), h + m + l = s to ~2^-24) arranged as operands of a bf16 MFMA that
+ * forms the scale products.  Activations take 6 bits per code plus 8 bytes per (row, group)
+ * and are padded to a multiple of 256 rows; weights take 6 bits per code plus 16 bytes per
+ * (column, group) and are padded to a multiple of 192 columns.  The buffers are opaque;
+ * sizes come from the *_bytes queries.  All buffers are device memory, 16-byte aligned,
+ * owned by the caller.
  *
  * svdq_act_packed_bytes / svdq_prepacked_weight_bytes: buffer sizes for `cfg` (INT4 only)
  *   and M rows.
@@ -167,8 +169,8 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
  * svdq_prepack_weight: wgt_codes [N, K/2] nibbles (full range [-8, 7]) + wgt_scales
  *   [N, K/64] fp32 -> prepacked, once per layer.
  * svdq_gemm_w4a4_packed: as svdq_gemm_w4a4 (INT4) on packed operands.  The result equals
- *   svdq_gemm_w4a4's up to fp32 rounding order and the hi/lo split of each scale product
- *   (relative error of one group's term below 2^-15).
+ *   svdq_gemm_w4a4's up to fp32 rounding order and the three-term split of each scale
+ *   product (relative error of one group's scale product a few fp32 ulp).
  * All enqueue on `stream`.
  */
 svdq_status svdq_act_packed_bytes(const svdq_layer_cfg* cfg, int64_t M, int64_t* bytes);
