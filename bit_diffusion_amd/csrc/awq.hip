@@ -54,9 +54,10 @@ __device__ __forceinline__ uint32_t awq_lds_addr(const void* p) {
 }
 // Global -> LDS copy of 1 KiB: lane l moves the 16 bytes at gaddr (its own address) to LDS
 // byte lds + 16 l.  Through asm, so that the compiler does not drain the copies before LDS
-// reads of other buffers; completion is tracked with awq_wait_vm.
+// reads of other buffers; completion is tracked with awq_wait_vm.  The s_nop is the wait
+// state an LDS DMA needs after an SALU write of M0.
 __device__ __forceinline__ void awq_dma(const void* gaddr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(gaddr), "s"(lds) : "memory");
 }
 

@@ -65,9 +65,10 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // 16 l) to LDS byte address lds + 16 l.  Issued through asm so that the compiler, which
 // cannot tell the DMA targets from the LDS buffers read meanwhile, does not drain every
 // DMA in flight before each LDS read; completion is tracked by wait_vm instead.  The asm
-// writes no VGPR (its result lands in LDS).
+// writes no VGPR (its result lands in LDS).  An LDS DMA that reads M0 right after an SALU
+// write of M0 needs one wait state (the s_nop).
 __device__ __forceinline__ void dma_chunk(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
 }
 

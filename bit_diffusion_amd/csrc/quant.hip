@@ -41,12 +41,15 @@ constexpr int kStep = 128;   // channels per wave step
 enum Mode { kInt4Nibbles = 0, kInt4Packed = 1, kNvfp4Nibbles = 2 };
 
 // Steps in flight per wave: the register budget (256 VGPRs at 8 waves per block) holds
-// three stages up to rank 16, two at rank 32 and one beyond; above rank 64 the L1 slice is
-// loaded when it is used.
+// three stages up to rank 32 (at rank 32 the third stage's L1 slice is loaded only after
+// the first stage is done, into the registers that stage freed) and one beyond; above
+// rank 64 the L1 slice is loaded when it is used.
 template <int RB>
-constexpr int kAhead = RB <= 1 ? 3 : RB == 2 ? 2 : 1;
+constexpr int kAhead = RB <= 2 ? 3 : 1;
 template <int RB>
 constexpr bool kPrefetchL1 = RB <= 4;
+template <int RB>
+constexpr bool kLateL1 = RB == 2;
 
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
@@ -62,15 +65,20 @@ __device__ __forceinline__ uint4 load_l1(const uint16_t* l1r, int K, int b, int 
 }
 
 template <int RB>
-__device__ __forceinline__ void load_stage(Stage<RB>& st, const uint16_t* xr, const uint16_t* l1r,
-                                           int K, int k0) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) st.x[t] = *reinterpret_cast<const uint4*>(xr + k0 + 8 * t);
+__device__ __forceinline__ void load_stage_l1(Stage<RB>& st, const uint16_t* l1r, int K, int k0) {
     if constexpr (kPrefetchL1<RB>)
 #pragma unroll
         for (int b = 0; b < RB; ++b)
 #pragma unroll
             for (int t = 0; t < 4; ++t) st.l1[4 * b + t] = load_l1(l1r, K, b, k0, t);
+}
+
+template <int RB>
+__device__ __forceinline__ void load_stage(Stage<RB>& st, const uint16_t* xr, const uint16_t* l1r,
+                                           int K, int k0, bool with_l1) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) st.x[t] = *reinterpret_cast<const uint4*>(xr + k0 + 8 * t);
+    if (with_l1) load_stage_l1<RB>(st, l1r, K, k0);
 }
 
 // The lane's 32 values in the order of the FP6 conversion: ev[i] is channel 2i (the low
@@ -315,7 +323,8 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
 #pragma unroll
         for (int s = 0; s < NA; ++s) {
             const int c = wave + kQWaves * min(it0 + s, nsw - 1);
-            load_stage<RB>(st[s], xr, l1r, K, min(c * kStep + 32 * q4, K - 32));
+            load_stage<RB>(st[s], xr, l1r, K, min(c * kStep + 32 * q4, K - 32),
+                           !(kLateL1<RB> && s == NA - 1));
         }
 #pragma unroll
         for (int s = 0; s < NA; ++s) *reinterpret_cast<uint2*>(&si_lds[wave][s][2 * lane]) = siv[s];
@@ -345,6 +354,10 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
                                 as_bf16x8(st[s].x[t]), as_bf16x8(w), acc[b], 0, 0, 0);
                         }
                 }
+            }
+            if (kLateL1<RB> && s == 0) {   // the last stage's L1 slice, into stage 0's registers
+                const int c = wave + kQWaves * min(it0 + NA - 1, nsw - 1);
+                load_stage_l1<RB>(st[NA - 1], l1r, K, min(c * kStep + 32 * q4, K - 32));
             }
         }
     }
