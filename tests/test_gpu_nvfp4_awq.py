@@ -36,8 +36,11 @@ def test_quant_nvfp4_shapes(M, K, r):
             gu.assert_lora_close(gu.host(lora), ol, xb, l1)
 
 
+# One 64-channel stage (K = 64), odd and even stage counts, several 256 x 192 tiles with
+# ragged row and column tails.
 @pytest.mark.parametrize("M,N,K,r,bias,act", [
     (1, 128, 64, 0, False, 0), (7, 96, 192, 16, True, 0), (130, 260, 512, 32, True, 1),
+    (300, 400, 1024, 32, True, 0), (513, 200, 640, 16, False, 1), (257, 193, 320, 0, True, 0),
 ])
 def test_gemm_nvfp4_shapes(M, N, K, r, bias, act):
     rng = np.random.default_rng(500 + M + N + K)
@@ -55,6 +58,27 @@ def test_gemm_nvfp4_shapes(M, N, K, r, bias, act):
     assert e <= 1e-5, e
     yb = gu.host(gu.gemm(ca, sa, cw, sw, lora, l2, b, act, True, "nvfp4", Sa, Sw))
     gu.assert_bf16_close(yb, ref)
+
+
+def test_gemm_nvfp4_unaligned_scales():
+    """E4M3 scale arrays at odd addresses are accepted (they take the reference kernel)."""
+    M, N, K, r = 70, 130, 256, 16
+    rng = np.random.default_rng(520)
+    ca, cw = synth.random_packed_nibbles(rng, M, K), synth.random_packed_nibbles(rng, N, K)
+    sa = rng.integers(0, 0x7F, size=(M, K // 16)).astype(np.uint8)
+    sw = rng.integers(0, 0x7F, size=(N, K // 16)).astype(np.uint8)
+    Sa, Sw = np.float32(0.002), np.float32(0.001)
+    lora, l2 = synth.random_bf16(rng, (M, r), 1.0), synth.random_bf16(rng, (N, r), 0.1)
+    ref = oracle.gemm_w4a4_nvfp4(ca, sa, Sa, cw, sw, Sw, lora, l2, None, 0)
+
+    def shifted(a):
+        buf = torch.zeros(a.size + 1, dtype=torch.uint8, device="cuda:0")
+        buf[1:] = gu.dev(a).reshape(-1)
+        return buf[1:].view(a.shape)
+
+    y = gu.host(gu.gemm(ca, shifted(sa), cw, shifted(sw), lora, l2, None, 0, precision="nvfp4",
+                        Sa=Sa, Sw=Sw))
+    assert gu.rel_fro(y, ref) <= 1e-5
 
 
 # M <= 4 with K a multiple of 512 up to 4096 runs the MFMA kernel, everything else the
