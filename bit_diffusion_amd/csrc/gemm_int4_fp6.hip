@@ -15,7 +15,12 @@
 // Both operands arrive in the layout of packed_layout.hpp (activations from
 // svdq_quantize_act_packed or svdq_pack_act, weights from svdq_prepack_weight), so a
 // pipeline stage is a plain copy: 26 KiB per (256x192 tile, group) moved global -> LDS by
-// the LDS-DMA path (global_load_lds_dwordx4), double-buffered in halves of three groups.
+// the LDS-DMA path (global_load_lds_dwordx4).  LDS holds a ring of three buffers of two
+// groups; while one buffer computes, the next one's copies land and the copies of the one
+// after are issued, spread over the computation.
+//
+// Per group and 32x32 tile the two MFMAs of the next tile are issued around the fmas of
+// the current one, so a wave keeps its MFMA pipe and its VALU busy at the same time.
 //
 // Tiling: 256x192 output tile per 512-thread workgroup, 8 waves as 4 x 2, each 64x96 =
 // 2 x 3 tiles of 32x32.  Workgroup ids are remapped so the workgroups an XCD runs at once
@@ -29,7 +34,7 @@ namespace {
 
 using namespace packed;
 
-constexpr int kThreads = 512, kStages = 6, kHalf = kStages / 2;
+constexpr int kThreads = 512, kStages = 6;   // 3 buffers of 2 groups
 constexpr int kStageBytes = kAStage + kBStage;   // 26624
 constexpr int kAChunks = kAStage / 1024;         // 14
 constexpr int kBChunks = kBStage / 1024;         // 12
@@ -61,6 +66,18 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)p);
 }
 
+// Wave-uniform values as SGPR operands of the DMA asm.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 // Global -> LDS DMA of one 1 KiB chunk: lane l moves the 16 bytes at sbase + voff (voff =
 // 16 l) to LDS byte address lds + 16 l.  Issued through asm so that the compiler, which
 // cannot tell the DMA targets from the LDS buffers read meanwhile, does not drain every
@@ -69,7 +86,15 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // write of M0 needs one wait state (the s_nop).
 __device__ __forceinline__ void dma_chunk(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory");
+                 :: "v"(voff), "s"(uniform_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+// The same under exec & mask (mask 0 or all ones, wave-uniform): with mask 0 no lane
+// accesses memory.  Code that waits on these counts them as if they were issued, which is
+// exact or one copy too strict either way.
+__device__ __forceinline__ void dma_chunk_m(const uint8_t* sbase, uint32_t voff, uint32_t lds, uint64_t mask) {
+    uint64_t saved;
+    asm volatile("s_mov_b32 m0, %2\n\ts_and_saveexec_b64 %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(uniform_u64(mask)), "s"(uniform_ptr(sbase)) : "memory", "scc");
 }
 
 __device__ __forceinline__ void tile_coords(int& pid_m, int& pid_n, int num_m, int num_n) {
@@ -110,8 +135,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     const uint32_t lds0 = lds_offset(smem);
     const uint32_t voff = lane * 16;
 
-    // Stage chunks: 0-13 activations, 14-25 weights.  Wave w copies chunks w, w + 8 and
-    // w + 16; waves 0 and 1 also chunks 24 and 25.
+    // One group's stage (start and tail of the pipeline): chunks 0-13 activations, 14-25
+    // weights.  Wave w copies chunks w, w + 8 and w + 16; waves 0 and 1 also 24 and 25.
     auto issue = [&](int h, int slot) {
         const uint8_t* ag = a_base + (int64_t)h * kAStage;
         const uint8_t* bg = b_base + (int64_t)h * kBStage;
@@ -123,9 +148,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         if (wave < 2) dma_chunk(bg + (wave + 24 - kAChunks) * 1024, voff, dst + (wave + 24) * 1024);
     };
 
-    // Double buffer of kHalf groups: one barrier per kHalf groups, after which the next
-    // kHalf groups' copies are issued into the half that was just consumed.  (A ring with a
-    // barrier every group serializes the copies with the arithmetic on gfx950.)
     const int fr = lane & 31, fh = lane >> 5;
     // byte selectors of v_perm_b32 (bytes 0-3: the l word, 4-7: the h | m << 16 word)
     const uint32_t psel0 = fh ? 0x07060100u : 0x05040504u;
@@ -133,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
 
     // The low-rank up-projection goes first: acc = lora_act . l2^T.  Its operand loads
     // (and the bias) are issued ahead of the first copies, so their latency hides behind
-    // the wait for the first half instead of standing in the epilogue.
+    // the wait for the first buffers instead of standing in the epilogue.
     const uint16_t* lora = (const uint16_t*)p.lora;
     const uint16_t* l2 = (const uint16_t*)p.l2;
     const int r = p.r;
@@ -160,7 +182,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         bv[j] = (bias && col < N) ? bf16_to_f32(bias[col]) : 0.0f;
     }
 
-    for (int h = 0; h < min(G, kHalf); ++h) issue(h, h);
+    // Buffer (third) t holds groups 2t and 2t + 1, 52 chunks: chunk c is chunk c % 26 of
+    // group 2t + c / 26.  Wave w copies chunks w + 8 j, j = 0..6 (j = 6 exists for w < 4
+    // only and is issued under an exec mask, so the loop below has no branches: branches
+    // there made the register allocator spill).
+    auto chunk_src = [&](int h0, int c) -> const uint8_t* {
+        const int k = c >= 26 ? 1 : 0;
+        const int cg = c - 26 * k;
+        const int h = h0 + k;
+        return cg < kAChunks ? a_base + (int64_t)h * kAStage + cg * 1024
+                             : b_base + (int64_t)h * kBStage + (cg - kAChunks) * 1024;
+    };
+    const uint64_t mask_lo4 = (wave < 4) ? ~0ull : 0ull;
+    auto issue_j = [&](int t, int j) {   // groups 2t and 2t + 1 both exist
+        const int c = wave + 8 * j;
+        const uint32_t dst = lds0 + (t % 3) * (2 * kStageBytes) + c * 1024;
+        if (j < 6) dma_chunk(chunk_src(2 * t, c), voff, dst);
+        else dma_chunk_m(chunk_src(2 * t, c), voff, dst, mask_lo4);
+    };
+    for (int h = 0; h < min(G, 4); ++h) issue(h, h);
 
     f32x16 acc[2][3];
 #pragma unroll
@@ -193,8 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     }
 
     // The operands of this wave for one group: two activation fragments and their scale
-    // operands, three weight fragments and theirs.  Within a half, the next group's
-    // operands are read from LDS while the current group computes.
+    // operands, three weight fragments and theirs.
     struct Frags {
         i32x8 a[2];
         bf16x4 ap[2];
@@ -224,43 +263,71 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
             f.wp[j] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(Bb + kFrag + lane * 8));
         }
     };
+    // Software-pipelined: the two MFMAs of pair q+1 are issued around the fmas of pair q,
+    // so the MFMA pipe and the VALU work at the same time within one wave.
     auto compute = [&](const Frags& f) {
+        f32x16 r0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[0], f.w[0], f32x16{}, 2, 2, 0, 127, 0, 127);
+        f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(f.ap[0], f.wp[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const f32x16 r = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    f.a[i], f.w[j], f32x16{}, 2, 2, 0, 127, 0, 127);
-                const f32x16 pp = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(f.ap[i], f.wp[j], f32x16{}, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(r[e], pp[e], acc[i][j][e]);
+        for (int q = 0; q < 6; ++q) {
+            const int i = q & 1, j = q >> 1;
+            f32x16 r1, p1;
+            if (q < 5) {
+                const int i1 = (q + 1) & 1, j1 = (q + 1) >> 1;
+                r1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i1], f.w[j1], f32x16{}, 2, 2, 0, 127, 0, 127);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i][j][e] = fmaf(r0[e], p0[e], acc[i][j][e]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q < 5) {
+                const int i1 = (q + 1) & 1, j1 = (q + 1) >> 1;
+                p1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(f.ap[i1], f.wp[j1], f32x16{}, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 8; e < 16; ++e) acc[i][j][e] = fmaf(r0[e], p0[e], acc[i][j][e]);
+            __builtin_amdgcn_sched_barrier(0);
+            r0 = r1;
+            p0 = p1;
+        }
     };
 
-    static_assert(kHalf == 3, "the unrolled half below is written for three groups");
-    const int g_full = G - G % kHalf;
-    for (int g0 = 0; g0 < g_full; g0 += kHalf) {
-        wait_vm<0>();   // this wave's copies of groups g0 .. g0+2 have landed
-        barrier();      // every wave's have; the other half is no longer read
-        const int h1 = min(G, g0 + 2 * kHalf);
-        for (int h = g0 + kHalf; h < h1; ++h) issue(h, h % kStages);
-
-        const uint8_t* S0 = smem + (g0 % kStages) * kStageBytes;
-        Frags f0, f1;
-        load_frags(S0, f0);
-        load_frags(S0 + kStageBytes, f1);
-        compute(f0);
-        __builtin_amdgcn_sched_barrier(0);   // keep groups apart (register pressure)
-        load_frags(S0 + 2 * kStageBytes, f0);
-        compute(f1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(f0);
-        __builtin_amdgcn_sched_barrier(0);
+    int t = 0;
+    for (; 2 * t + 5 < G; ++t) {   // the third two ahead (groups 2t+4, 2t+5) exists
+        wait_vm<6>();   // this wave's copies of third t have landed (third t+1's may not)
+        barrier();      // every wave's have; third t-1's buffer is no longer read
+        const uint8_t* S = smem + (t % 3) * (2 * kStageBytes);
+        {
+            Frags f;
+            load_frags(S, f);
+            compute(f);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) issue_j(t + 2, j);   // third t+2's copies, spread over the third
+        {
+            Frags f;
+            load_frags(S + kStageBytes, f);
+            compute(f);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 3; j < 7; ++j) issue_j(t + 2, j);
     }
-    if (g_full < G) {   // the last G % 3 groups
+    // tail: thirds t and t+1 are issued; at most one group (2t+4 = G-1) is not
+    wait_vm<0>();
+    barrier();
+    for (int h = 2 * t + 4; h < G; ++h) issue(h, h % kStages);
+    for (int g = 2 * t; g < min(G, 2 * t + 2); ++g) {
+        Frags f;
+        load_frags(smem + (g % kStages) * kStageBytes, f);
+        compute(f);
+    }
+    if (2 * t + 2 < G) {
         wait_vm<0>();
         barrier();
-        for (int g = g_full; g < G; ++g) {
+        for (int g = 2 * t + 2; g < G; ++g) {
             Frags f;
             load_frags(smem + (g % kStages) * kStageBytes, f);
             compute(f);
