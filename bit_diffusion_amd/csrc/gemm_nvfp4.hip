@@ -12,12 +12,12 @@
 // LDS and contracted with the 16-bit MFMA in fp32; S_a * S_w is applied in the epilogue.
 //
 // Fast kernel (gemm_nvfp4_f16_kernel): 256x192 output tile per 512-thread workgroup, 8
-// waves as 4 x 2 of 64x96.  Codes and scale bytes of a 64-channel stage are copied to LDS
-// by LDS DMA, three stages deep.  Per stage every thread converts one 32-code half row of
-// A (and of B for threads < 384): v_cvt_scalef32_pk_f16_fp4 (scale 1) turns a code byte
-// into two exact f16 values and v_pk_mul_f16 applies the block scale (exact).  The f16
-// rows go to a double-buffered, XOR-swizzled LDS tile and v_mfma_f32_32x32x16_f16
-// contracts.  One barrier per stage.
+// waves as 4 x 2 of 64x96.  Codes and scale bytes go to LDS by LDS DMA in stages of 256
+// channels (128 contiguous bytes of codes per row: whole cache lines), double-buffered,
+// one barrier per stage.  Each wave converts the operands of its own MFMA fragments per
+// 16-channel k-step: v_cvt_scalef32_pk_f16_fp4 (scale 1) turns a code byte into two exact
+// f16 values and v_pk_mul_f16 applies the block scale (exact); v_mfma_f32_32x32x16_f16
+// contracts.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -171,27 +171,20 @@ __global__ __launch_bounds__(kThreads) void gemm_nvfp4_v0_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------- fast kernel
-constexpr int kFM = 256, kFN = 192, kFK = 64, kFThreads = 512;
-// f16 tile of one stage: rows of 64 values (128 bytes), 16-byte chunk c of row r stored at
-// chunk position c ^ (r & 7) so that 32 consecutive rows read one chunk conflict-free.
-constexpr int kFTile = (kFM + kFN) * 128;                      // 57344 bytes
-// raw stage as copied from global memory: codes (row r, 16-byte half h at slot 2r + h), then
-// the scale dword of every row
-constexpr int kRawA = kFM * 32, kRawB = kFN * 32;               // 8192, 6144
-constexpr int kRawSA = kFM * 4, kRawSB = kFN * 4;               // 1024, 768
-constexpr int kRaw = kRawA + kRawB + kRawSA + kRawSB;           // 16128
-constexpr int kRawStages = 3;
-constexpr int kFSmemBytes = 2 * kFTile + kRawStages * kRaw;     // 163072
+constexpr int kFM = 256, kFN = 192, kFThreads = 512;
+constexpr int kFK = 256;                        // channels per pipeline stage
+// One stage in LDS: codes of every row (128 bytes: 8 chunks of 16 bytes, chunk c of row r
+// stored at position c ^ ((r >> 1) & 7) so that a fragment's 32 rows read one chunk
+// conflict-free), then the E4M3 scale bytes as [sub-stage u][row][4] (64 channels = 4
+// blocks per u).
+constexpr int kCA = kFM * 128, kCB = kFN * 128;             // 32768, 24576
+constexpr int kSA = 4 * kFM * 4, kSB = 4 * kFN * 4;         // 4096, 3072
+constexpr int kFStage = kCA + kCB + kSA + kSB;              // 64512
+constexpr int kFSmemBytes = 2 * kFStage;                    // 129024
 static_assert(kFSmemBytes <= 160 * 1024, "LDS budget");
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-template <int n>
-__device__ __forceinline__ void fwait_vm() {
-    static_assert(n >= 0 && n < 16, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0070 | n);   // vmcnt = n, lgkmcnt = 0 (expcnt not waited)
-}
 
 __device__ __forceinline__ void fbarrier() {
     asm volatile("" ::: "memory");
@@ -203,7 +196,7 @@ typedef __attribute__((address_space(3))) uint8_t flds_u8;
 
 // Global -> LDS copies (LDS DMA): lane l moves 16 (x4) or 4 (dword) bytes from its own
 // global address to LDS byte lds + 16 l (+ 4 l).  The s_nop is the wait state an LDS DMA
-// needs after an SALU write of M0.  Completion is tracked with fwait_vm.
+// needs after an SALU write of M0.  Completion: s_waitcnt vmcnt(0) before the barrier.
 __device__ __forceinline__ void fdma_x4(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(g), "s"(lds) : "memory");
@@ -213,25 +206,19 @@ __device__ __forceinline__ void fdma_x1(const void* g, uint32_t lds) {
                  :: "v"(g), "s"(lds) : "memory");
 }
 
-// 32 codes (16 bytes, code 2i in the low nibble of byte i) times the E4M3 scales sc0 (codes
-// 0-15) and sc1 (16-31): 32 exact f16 products, returned as 16 words.
-__device__ __forceinline__ void dequant32h(uint4 c, uint32_t sc, uint32_t (&o)[16]) {
-    const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
-    const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
-    const f16x2 v0 = {s0, s0}, v1 = {s1, s1};
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        f16x2 h;
-        switch (i & 3) {
-            case 0: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i >> 2], 1.0f, 0); break;
-            case 1: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i >> 2], 1.0f, 1); break;
-            case 2: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i >> 2], 1.0f, 2); break;
-            default: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i >> 2], 1.0f, 3); break;
-        }
-        h = h * (i < 8 ? v0 : v1);
-        o[i] = __builtin_bit_cast(uint32_t, h);
-    }
+// 8 codes (a dword, code 2i in the low nibble of byte i) times the E4M3 scale sc as an
+// exact f16 MFMA operand.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 sc) {
+    const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
+    const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
+    const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
+    const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
+    return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+__device__ __forceinline__ f16x2 scale_pair(uint32_t sc, int byte) {
+    const _Float16 v = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)(sc >> (8 * byte)), 0);
+    return f16x2{v, v};
 }
 
 __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p) {
@@ -240,69 +227,58 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = p.M;
-    const int N = p.N, K = p.K, S = K / kFK;
+    const int N = p.N, K = p.K;
+    const int S = (K + kFK - 1) / kFK;            // stages (the last may cover 64..192 channels)
     const int64_t num_m = (M + kFM - 1) / kFM;
     const int num_n = (N + kFN - 1) / kFN;
-    // tiles in row-major order, workgroups of one XCD (ids congruent mod 8) on a contiguous
-    // range of them when the count allows
+    // tiles in row-major order; the workgroups of one XCD (ids congruent mod 8) take a
+    // contiguous range of them when the count allows
     int64_t t = blockIdx.x;
     const int64_t nt = num_m * num_n;
     if ((nt & 7) == 0) t = (t & 7) * (nt >> 3) + (t >> 3);
     const int64_t m0 = (t / num_n) * kFM;
     const int n0 = (int)(t % num_n) * kFN;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(flds_u8*)fsm);
-    const uint32_t raw0 = lds0 + 2 * kFTile;
 
-    // ---- copy issue: 21 DMAs per stage, wave w takes numbers w, w + 8, w + 16 (< 21):
-    // 0-7 A codes, 8-13 B codes, 14-17 A scales, 18-20 B scales
     const uint8_t* acodes = (const uint8_t*)p.acodes;
     const uint8_t* wcodes = (const uint8_t*)p.wcodes;
     const uint8_t* ascales = (const uint8_t*)p.ascales;
     const uint8_t* wscales = (const uint8_t*)p.wscales;
-    auto issue_one = [&](int d, int s, uint32_t raw) {
-        if (d < 8) {                      // A codes, slots 64 d + lane
-            const int slot = 64 * d + lane, row = slot >> 1;
-            const int64_t m = min(m0 + row, M - 1);
-            fdma_x4(acodes + m * (K / 2) + s * 32 + 16 * (slot & 1), raw + 1024 * d);
-        } else if (d < 14) {              // B codes
-            const int slot = 64 * (d - 8) + lane, row = slot >> 1;
-            const int n = min(n0 + row, N - 1);
-            fdma_x4(wcodes + (int64_t)n * (K / 2) + s * 32 + 16 * (slot & 1), raw + kRawA + 1024 * (d - 8));
-        } else if (d < 18) {              // A scales, rows 64 (d - 14) + lane
-            const int64_t m = min(m0 + 64 * (d - 14) + lane, M - 1);
-            fdma_x1(ascales + m * (K / 16) + s * 4, raw + kRawA + kRawB + 256 * (d - 14));
-        } else {                          // B scales
-            const int n = min(n0 + 64 * (d - 18) + lane, N - 1);
-            fdma_x1(wscales + (int64_t)n * (K / 16) + s * 4, raw + kRawA + kRawB + kRawSA + 256 * (d - 18));
-        }
-    };
-    // DMAs per stage of this wave: 3 for waves 0-4, 2 for waves 5-7
-    auto issue = [&](int s) {
-        const uint32_t raw = raw0 + (s % kRawStages) * kRaw;
-        issue_one(wave, s, raw);
-        issue_one(wave + 8, s, raw);
-        if (wave + 16 < 21) issue_one(wave + 16, s, raw);
-    };
 
-    // ---- conversion: thread t converts half (t & 1) of A row t >> 1 and, for t < 384, of
-    // B row t >> 1, from the raw stage to the f16 tile
-    const int lr = tid >> 1, lh = tid & 1;
-    auto convert_one = [&](const uint8_t* codes, const uint8_t* sc4, uint8_t* row) {
-        const uint4 c = *reinterpret_cast<const uint4*>(codes);
-        const uint32_t sc = *reinterpret_cast<const uint32_t*>(sc4) >> (16 * lh);
-        uint32_t o[16];
-        dequant32h(c, sc, o);
+    // ---- copies of stage s: 56 code copies (8 rows x 128 bytes each: 32 for A, 24 for B)
+    // and 4 x 7 scale copies (one dword per row and 64-channel sub-stage: 64 rows each);
+    // wave w issues numbers w, w + 8, ...
+    auto issue = [&](int s) {
+        const uint32_t base = lds0 + (s & 1) * kFStage;
+        const int kc = s * kFK;                       // first channel of the stage
+        const int nsub = min(4, (K - kc) / 64);       // valid 64-channel sub-stages
+        const int nchunk = 2 * nsub;                  // valid 16-byte chunks per row
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint4*>(row + 16 * ((4 * lh + q) ^ (lr & 7))) =
-                make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-    };
-    auto convert = [&](int s, int buf) {
-        const uint8_t* raw = fsm + 2 * kFTile + (s % kRawStages) * kRaw;
-        uint8_t* tile = fsm + buf * kFTile;
-        convert_one(raw + 16 * tid, raw + kRawA + kRawB + 4 * lr, tile + lr * 128);
-        if (tid < 2 * kFN)
-            convert_one(raw + kRawA + 16 * tid, raw + kRawA + kRawB + kRawSA + 4 * lr, tile + (kFM + lr) * 128);
+        for (int q = 0; q < 11; ++q) {
+            const int d = wave + 8 * q;
+            if (d < 56) {
+                const bool isa = d < 32;
+                const int j = isa ? d : d - 32;
+                const int row = 8 * j + (lane >> 3), pos = lane & 7;
+                const int c = pos ^ ((row >> 1) & 7);
+                const int cc = c < nchunk ? c : 0;    // chunks past K: any valid address
+                const uint8_t* src = isa ? acodes + min(m0 + row, M - 1) * (K / 2)
+                                         : wcodes + (int64_t)min(n0 + row, N - 1) * (K / 2);
+                fdma_x4(src + kc / 2 + 16 * cc, base + (isa ? 0 : kCA) + 1024 * j);
+            } else if (d < 84) {
+                const int e = d - 56;                 // 0-27: 4 sub-stages x (4 A + 3 B)
+                const int u = e / 7, v = e % 7;
+                if (u < nsub) {
+                    const bool isa = v < 4;
+                    const int row = 64 * (isa ? v : v - 4) + lane;
+                    const uint8_t* src = isa ? ascales + min(m0 + row, M - 1) * (K / 16)
+                                             : wscales + (int64_t)min(n0 + row, N - 1) * (K / 16);
+                    const uint32_t dst = base + kCA + kCB + (isa ? u * kFM * 4 + 256 * v
+                                                                 : kSA + u * kFN * 4 + 256 * (v - 4));
+                    fdma_x1(src + kc / 16 + 4 * u, dst);
+                }
+            }
+        }
     };
 
     f32x16 acc[2][3];
@@ -313,45 +289,62 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // ---- compute one 64-channel sub-stage u of stage buffer b.  The MFMA contracts any
+    // consistent permutation of the channels: for k-step kk, lane half h supplies codes
+    // 8 (4h + kk) .. + 7 of the sub-stage, i.e. dword kk of its 16-byte chunk 2u + h, in
+    // block 2h + kk / 2.
     const int fr = lane & 31, fh = lane >> 5;
-    auto compute = [&](int buf) {
-        const uint8_t* A = fsm + buf * kFTile + (wm * 64 + fr) * 128;
-        const uint8_t* B = fsm + buf * kFTile + (kFM + wn * 96 + fr) * 128;
-        const int sw = fr & 7;   // rows of a fragment start at multiples of 8
+    auto compute = [&](int b, int u) {
+        const uint8_t* st = fsm + b * kFStage;
+        uint4 ca[2], cb[3];
+        f16x2 sa[2][2], sb[3][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = wm * 64 + 32 * i + fr;
+            ca[i] = *reinterpret_cast<const uint4*>(st + row * 128 + 16 * ((2 * u + fh) ^ ((row >> 1) & 7)));
+            const uint32_t sc = *reinterpret_cast<const uint32_t*>(st + kCA + kCB + u * kFM * 4 + 4 * row);
+            sa[i][0] = scale_pair(sc, 2 * fh);
+            sa[i][1] = scale_pair(sc, 2 * fh + 1);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int row = wn * 96 + 32 * j + fr;
+            cb[j] = *reinterpret_cast<const uint4*>(st + kCA + row * 128 + 16 * ((2 * u + fh) ^ ((row >> 1) & 7)));
+            const uint32_t sc = *reinterpret_cast<const uint32_t*>(st + kCA + kCB + kSA + u * kFN * 4 + 4 * row);
+            sb[j][0] = scale_pair(sc, 2 * fh);
+            sb[j][1] = scale_pair(sc, 2 * fh + 1);
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int pos = 16 * ((2 * kk + fh) ^ sw);
-            f16x8 a[2], b[3];
+            f16x8 a[2], bb[3];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const f16x8*>(A + i * 32 * 128 + pos);
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t w = kk == 0 ? ca[i].x : kk == 1 ? ca[i].y : kk == 2 ? ca[i].z : ca[i].w;
+                a[i] = dequant8(w, sa[i][kk >> 1]);
+            }
 #pragma unroll
-            for (int j = 0; j < 3; ++j) b[j] = *reinterpret_cast<const f16x8*>(B + j * 32 * 128 + pos);
+            for (int j = 0; j < 3; ++j) {
+                const uint32_t w = kk == 0 ? cb[j].x : kk == 1 ? cb[j].y : kk == 2 ? cb[j].z : cb[j].w;
+                bb[j] = dequant8(w, sb[j][kk >> 1]);
+            }
 #pragma unroll
             for (int j = 0; j < 3; ++j)
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
     };
 
-    // ---- pipeline: raw stages s+1, s+2 in flight while stage s computes; per stage one
-    // barrier, after which stage s+1 is converted into the other f16 buffer and the copies of
-    // stage s+3 go into the raw buffer stage s just released.
+    // ---- pipeline: two stage buffers; stage s + 1 is copied while stage s computes
     issue(0);
-    if (S > 1) issue(1);
-    if (S > 2) issue(2);
-    fwait_vm<0>();
-    fbarrier();
-    convert(0, 0);
     for (int s = 0; s < S; ++s) {
-        // this wave's copies of stage s + 1 have landed: at most stage s + 2's (2 or 3) remain
-        if (s + 2 < S) fwait_vm<2>();
-        else fwait_vm<0>();
-        fbarrier();   // every wave's have; stage s's f16 tile is complete; raw s is free
-        if (s + 3 < S) issue(s + 3);
-        if (s + 1 < S) convert(s + 1, (s + 1) & 1);
-        compute(s & 1);
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0): this wave's copies of s landed
+        fbarrier();                           // every wave's have; buffer (s + 1) & 1 is free
+        if (s + 1 < S) issue(s + 1);
+        const int nsub = min(4, (K - s * kFK) / 64);
+        for (int u = 0; u < nsub; ++u) compute(s & 1, u);
     }
+
     // ---- epilogue: S_a S_w, low-rank branch, bias, GELU, store
     const float sasw = p.Sa * p.Sw;
 #pragma unroll
@@ -408,7 +401,7 @@ bool gemm_nvfp4_init() {
 }
 
 void launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
-    // The fast kernel reads 16-byte code pieces and the 4 scale bytes of a row's stage.
+    // The fast kernel copies 16-byte code pieces and the scale dword of a row's 64 channels.
     const bool fast = (reinterpret_cast<uintptr_t>(a.acodes) % 16) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.wcodes) % 16) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.ascales) % 4) == 0 &&
