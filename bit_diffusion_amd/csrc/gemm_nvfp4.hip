@@ -175,10 +175,9 @@ constexpr int kFM = 256, kFN = 192, kFThreads = 512;
 constexpr int kFK = 256;                        // channels per pipeline stage
 // One stage in LDS: codes of every row (128 bytes: 8 chunks of 16 bytes, chunk c of row r
 // stored at position c ^ ((r >> 1) & 7) so that a fragment's 32 rows read one chunk
-// conflict-free), then the E4M3 scale bytes as [sub-stage u][row][4] (64 channels = 4
-// blocks per u).
+// conflict-free), then the 16 E4M3 scale bytes of every row.  K is a multiple of 256.
 constexpr int kCA = kFM * 128, kCB = kFN * 128;             // 32768, 24576
-constexpr int kSA = 4 * kFM * 4, kSB = 4 * kFN * 4;         // 4096, 3072
+constexpr int kSA = kFM * 16, kSB = kFN * 16;               // 4096, 3072
 constexpr int kFStage = kCA + kCB + kSA + kSB;              // 64512
 constexpr int kFSmemBytes = 2 * kFStage;                    // 129024
 static_assert(kFSmemBytes <= 160 * 1024, "LDS budget");
@@ -228,7 +227,7 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = p.M;
     const int N = p.N, K = p.K;
-    const int S = (K + kFK - 1) / kFK;            // stages (the last may cover 64..192 channels)
+    const int S = K / kFK;
     const int64_t num_m = (M + kFM - 1) / kFM;
     const int num_n = (N + kFN - 1) / kFN;
     // tiles in row-major order; the workgroups of one XCD (ids congruent mod 8) take a
@@ -246,37 +245,29 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
     const uint8_t* wscales = (const uint8_t*)p.wscales;
 
     // ---- copies of stage s: 56 code copies (8 rows x 128 bytes each: 32 for A, 24 for B)
-    // and 4 x 7 scale copies (one dword per row and 64-channel sub-stage: 64 rows each);
-    // wave w issues numbers w, w + 8, ...
+    // and 7 scale copies (16 bytes per row, 64 rows each: 4 for A, 3 for B); wave w issues
+    // numbers w, w + 8, ...
     auto issue = [&](int s) {
         const uint32_t base = lds0 + (s & 1) * kFStage;
         const int kc = s * kFK;                       // first channel of the stage
-        const int nsub = min(4, (K - kc) / 64);       // valid 64-channel sub-stages
-        const int nchunk = 2 * nsub;                  // valid 16-byte chunks per row
 #pragma unroll
-        for (int q = 0; q < 11; ++q) {
+        for (int q = 0; q < 8; ++q) {
             const int d = wave + 8 * q;
             if (d < 56) {
                 const bool isa = d < 32;
                 const int j = isa ? d : d - 32;
                 const int row = 8 * j + (lane >> 3), pos = lane & 7;
                 const int c = pos ^ ((row >> 1) & 7);
-                const int cc = c < nchunk ? c : 0;    // chunks past K: any valid address
                 const uint8_t* src = isa ? acodes + min(m0 + row, M - 1) * (K / 2)
                                          : wcodes + (int64_t)min(n0 + row, N - 1) * (K / 2);
-                fdma_x4(src + kc / 2 + 16 * cc, base + (isa ? 0 : kCA) + 1024 * j);
-            } else if (d < 84) {
-                const int e = d - 56;                 // 0-27: 4 sub-stages x (4 A + 3 B)
-                const int u = e / 7, v = e % 7;
-                if (u < nsub) {
-                    const bool isa = v < 4;
-                    const int row = 64 * (isa ? v : v - 4) + lane;
-                    const uint8_t* src = isa ? ascales + min(m0 + row, M - 1) * (K / 16)
-                                             : wscales + (int64_t)min(n0 + row, N - 1) * (K / 16);
-                    const uint32_t dst = base + kCA + kCB + (isa ? u * kFM * 4 + 256 * v
-                                                                 : kSA + u * kFN * 4 + 256 * (v - 4));
-                    fdma_x1(src + kc / 16 + 4 * u, dst);
-                }
+                fdma_x4(src + kc / 2 + 16 * c, base + (isa ? 0 : kCA) + 1024 * j);
+            } else if (d < 63) {
+                const int v = d - 56;                 // 0-3 A, 4-6 B
+                const bool isa = v < 4;
+                const int row = 64 * (isa ? v : v - 4) + lane;
+                const uint8_t* src = isa ? ascales + min(m0 + row, M - 1) * (K / 16)
+                                         : wscales + (int64_t)min(n0 + row, N - 1) * (K / 16);
+                fdma_x4(src + kc / 16, base + kCA + kCB + (isa ? 1024 * v : kSA + 1024 * (v - 4)));
             }
         }
     };
@@ -296,13 +287,14 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
     const int fr = lane & 31, fh = lane >> 5;
     auto compute = [&](int b, int u) {
         const uint8_t* st = fsm + b * kFStage;
+        const int su = 4 * u;   // this sub-stage's 4 scale bytes within the row's 16
         uint4 ca[2], cb[3];
         f16x2 sa[2][2], sb[3][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int row = wm * 64 + 32 * i + fr;
             ca[i] = *reinterpret_cast<const uint4*>(st + row * 128 + 16 * ((2 * u + fh) ^ ((row >> 1) & 7)));
-            const uint32_t sc = *reinterpret_cast<const uint32_t*>(st + kCA + kCB + u * kFM * 4 + 4 * row);
+            const uint32_t sc = *reinterpret_cast<const uint32_t*>(st + kCA + kCB + 16 * row + su);
             sa[i][0] = scale_pair(sc, 2 * fh);
             sa[i][1] = scale_pair(sc, 2 * fh + 1);
         }
@@ -310,7 +302,7 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
         for (int j = 0; j < 3; ++j) {
             const int row = wn * 96 + 32 * j + fr;
             cb[j] = *reinterpret_cast<const uint4*>(st + kCA + row * 128 + 16 * ((2 * u + fh) ^ ((row >> 1) & 7)));
-            const uint32_t sc = *reinterpret_cast<const uint32_t*>(st + kCA + kCB + kSA + u * kFN * 4 + 4 * row);
+            const uint32_t sc = *reinterpret_cast<const uint32_t*>(st + kCA + kCB + kSA + 16 * row + su);
             sb[j][0] = scale_pair(sc, 2 * fh);
             sb[j][1] = scale_pair(sc, 2 * fh + 1);
         }
@@ -341,8 +333,8 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
         __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0): this wave's copies of s landed
         fbarrier();                           // every wave's have; buffer (s + 1) & 1 is free
         if (s + 1 < S) issue(s + 1);
-        const int nsub = min(4, (K - s * kFK) / 64);
-        for (int u = 0; u < nsub; ++u) compute(s & 1, u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) compute(s & 1, u);
     }
 
     // ---- epilogue: S_a S_w, low-rank branch, bias, GELU, store
@@ -401,11 +393,12 @@ bool gemm_nvfp4_init() {
 }
 
 void launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
-    // The fast kernel copies 16-byte code pieces and the scale dword of a row's 64 channels.
-    const bool fast = (reinterpret_cast<uintptr_t>(a.acodes) % 16) == 0 &&
+    // The fast kernel copies 16-byte pieces of codes and scales: K a multiple of 256 and
+    // 16-byte aligned arrays.
+    const bool fast = a.K % kFK == 0 && (reinterpret_cast<uintptr_t>(a.acodes) % 16) == 0 &&
                       (reinterpret_cast<uintptr_t>(a.wcodes) % 16) == 0 &&
-                      (reinterpret_cast<uintptr_t>(a.ascales) % 4) == 0 &&
-                      (reinterpret_cast<uintptr_t>(a.wscales) % 4) == 0;
+                      (reinterpret_cast<uintptr_t>(a.ascales) % 16) == 0 &&
+                      (reinterpret_cast<uintptr_t>(a.wscales) % 16) == 0;
     const int64_t num_m = (a.M + kFM - 1) / kFM;
     const int num_n = (a.N + kFN - 1) / kFN;
     if (fast && num_m * num_n < ((int64_t)1 << 31) && gemm_nvfp4_init()) {

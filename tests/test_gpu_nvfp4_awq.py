@@ -36,11 +36,12 @@ def test_quant_nvfp4_shapes(M, K, r):
             gu.assert_lora_close(gu.host(lora), ol, xb, l1)
 
 
-# One 64-channel stage (K = 64), odd and even stage counts, several 256 x 192 tiles with
-# ragged row and column tails.
+# K a multiple of 256 takes the fast kernel (two, three and four 256-channel stages over
+# several 256 x 192 tiles with ragged row and column tails); other K the reference kernel.
 @pytest.mark.parametrize("M,N,K,r,bias,act", [
     (1, 128, 64, 0, False, 0), (7, 96, 192, 16, True, 0), (130, 260, 512, 32, True, 1),
     (300, 400, 1024, 32, True, 0), (513, 200, 640, 16, False, 1), (257, 193, 320, 0, True, 0),
+    (70, 500, 768, 16, True, 1), (1, 20, 256, 0, False, 0),
 ])
 def test_gemm_nvfp4_shapes(M, N, K, r, bias, act):
     rng = np.random.default_rng(500 + M + N + K)
@@ -61,7 +62,8 @@ def test_gemm_nvfp4_shapes(M, N, K, r, bias, act):
 
 
 def test_gemm_nvfp4_unaligned_scales():
-    """E4M3 scale arrays at odd addresses are accepted (they take the reference kernel)."""
+    """E4M3 scale arrays that are not 16-byte aligned are accepted (they take the reference
+    kernel)."""
     M, N, K, r = 70, 130, 256, 16
     rng = np.random.default_rng(520)
     ca, cw = synth.random_packed_nibbles(rng, M, K), synth.random_packed_nibbles(rng, N, K)
