@@ -9,6 +9,10 @@ of 64, bf16 bias, bf16 output.
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline] [--only-main]
     python bench.py --copy-calibration      # plain 256 MiB device copies (counter calibration)
 
+The timed region is one replay of a HIP graph that holds exactly `--steps` steps (captured
+after the warmup, replayed once untimed, checked against an eager step); the same steps
+launched eagerly are reported as `ms_per_step_eager`.
+
 Prints one JSON line.  `value` is TOPS of the linear, counting 2MNK + 2MNr + 2MKr
 operations per step (the low-rank branch's flops included, the dense bf16 work the method
 avoids not counted), with every input already in HBM.  Inputs rotate through enough copies
@@ -195,7 +199,7 @@ def make_inputs(copies):
     Activations: the workload's draw (bf16 N(0,1), 31 outlier channels x50).  Smoothing
     factors from the activation and weight column maxima.  The 4-bit residual weights are
     produced by this library's own activation kernel from a synthetic bf16 residual (the
-    GEMM's speed does not depend on the code values).  Low-rank factors: bf16 N(0, 0.02).
+    GEMM's speed does not depend on the code values).  Low-rank factors: bf16 N(0, 0.02), the down-projection factor prepacked once like the weights.
     """
     import torch
     import synth
@@ -238,6 +242,9 @@ def make_inputs(copies):
             lora=torch.empty((M, R), dtype=torch.int16, device=dev),
             out=torch.empty((M, N), dtype=torch.int16, device=dev),
         )
+        cfg_r = bd.LayerCfg.make(K, N, R)
+        s["l1p"] = torch.empty(bd.svdq_prepacked_l1_bytes(cfg_r), dtype=torch.uint8, device=dev)
+        bd.svdq_prepack_l1(cfg_r, s["l1"], s["l1p"])
         sets.append(s)
     torch.cuda.synchronize()
     return si, sets, d
@@ -287,43 +294,62 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    def quant(s):
-        bd.svdq_quantize_act_packed(cfg, M, s["x"], si, s["l1"], s["apacked"], s["scales"],
-                                    s["lora"], sp)
+    def quant(s, st=sp):
+        bd.svdq_quantize_act_packed(cfg, M, s["x"], si, s["l1p"], s["apacked"], s["scales"],
+                                    s["lora"], st)
 
-    def gemm(s):
+    def gemm(s, st=sp):
         bd.svdq_gemm_w4a4_packed(cfg, M, s["apacked"], s["packed"], s["lora"], s["l2"],
-                                 s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16, s["out"], sp)
+                                 s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16, s["out"], st)
 
-    def step(s):
-        quant(s)
-        gemm(s)
+    def step(s, st=sp):
+        quant(s, st)
+        gemm(s, st)
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
-
-    # whole-step timing
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # eager launches, for reference
     ev0.record(stream)
     for i in range(args.steps):
         step(sets[i % len(sets)])
     ev1.record(stream)
     torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_eager = ev0.elapsed_time(ev1) / args.steps
 
-    # per-kernel timing (events between the two launches of each step)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
-    for i in range(args.steps):
-        s = sets[i % len(sets)]
-        evs[3 * i].record(stream)
-        quant(s)
-        evs[3 * i + 1].record(stream)
-        gemm(s)
-        evs[3 * i + 2].record(stream)
+    # whole-step timing: the `steps` steps captured once into a HIP graph (capturing runs
+    # nothing) and replayed, as a denoising loop launches its layers; one untimed replay
+    # first (the graph's first launch uploads it)
+    cs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(graph, stream=cs):
+            for i in range(args.steps):
+                step(sets[i % len(sets)], cs.cuda_stream)
     torch.cuda.synchronize()
-    t_q = np.array([evs[3 * i].elapsed_time(evs[3 * i + 1]) for i in range(args.steps)])
-    t_g = np.array([evs[3 * i + 1].elapsed_time(evs[3 * i + 2]) for i in range(args.steps)])
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    # the replayed graph computes what eager launches compute (same inputs, deterministic
+    # kernels): the last graph step on set j against one eager step on it
+    j = (args.steps - 1) % len(sets)
+    from_graph = sets[j]["out"].clone()
+    step(sets[j])
+    torch.cuda.synchronize()
+    if not torch.equal(from_graph, sets[j]["out"]):
+        raise RuntimeError("graph replay and eager launch disagree")
+
+    # per-kernel timing: each kernel launched `steps` times back to back over the rotating
+    # input sets, one event pair around the batch on the launching stream (an event pair
+    # around every launch would add the event packets' own latency to each kernel)
+    t_q = np.array(time_launches(lambda i: quant(sets[i % len(sets)]), args.steps, stream))
+    t_g = np.array(time_launches(lambda i: gemm(sets[i % len(sets)]), args.steps, stream))
 
     ops_gemm = 2.0 * M * N * K + 2.0 * M * N * R
     ops_total = ops_gemm + 2.0 * M * K * R
@@ -344,6 +370,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_eager": round(ms_eager, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

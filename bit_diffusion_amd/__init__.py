@@ -19,6 +19,7 @@ __all__ = [
     "svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_device",
     "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
     "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
+    "svdq_prepacked_l1_bytes", "svdq_prepack_l1",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -85,10 +86,21 @@ def svdq_prepacked_weight_bytes(cfg):
     return n.value
 
 
-def svdq_quantize_act_packed(cfg, M, x, smooth_inv, l1, act_packed, act_scales, lora_act,
+def svdq_prepacked_l1_bytes(cfg):
+    n = ctypes.c_int64(0)
+    _check(lib().svdq_prepacked_l1_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def svdq_prepack_l1(cfg, l1, l1_packed, stream=None):
+    return _check(lib().svdq_prepack_l1(ctypes.byref(cfg), _ptr(l1), _ptr(l1_packed),
+                                        _stream(stream)))
+
+
+def svdq_quantize_act_packed(cfg, M, x, smooth_inv, l1_packed, act_packed, act_scales, lora_act,
                              stream=None):
     return _check(lib().svdq_quantize_act_packed(
-        ctypes.byref(cfg), int(M), _ptr(x), _ptr(smooth_inv), _ptr(l1), _ptr(act_packed),
+        ctypes.byref(cfg), int(M), _ptr(x), _ptr(smooth_inv), _ptr(l1_packed), _ptr(act_packed),
         _ptr(act_scales), _ptr(lora_act), _stream(stream)))
 
 

@@ -25,7 +25,8 @@ SVDQ_ACT_GELU_TANH = 1
 EXPORTS = ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_device",
            "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version",
            "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
-           "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed")
+           "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
+           "svdq_prepacked_l1_bytes", "svdq_prepack_l1")
 
 
 class LayerCfg(ctypes.Structure):
@@ -69,6 +70,8 @@ def lib():
         L.svdq_quantize_act_packed.argtypes = [cfgp, I64, P, P, P, P, P, P, P]
         L.svdq_pack_act.argtypes = [cfgp, I64, P, P, P, P]
         L.svdq_prepack_weight.argtypes = [cfgp, P, P, P, P]
+        L.svdq_prepacked_l1_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_int64)]
+        L.svdq_prepack_l1.argtypes = [cfgp, P, P, P]
         L.svdq_gemm_w4a4_packed.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P]
         L.svdq_check_device.argtypes = [ctypes.c_int]
         L.svdq_check_arch.argtypes = [ctypes.c_char_p]
@@ -80,7 +83,8 @@ def lib():
         for name in ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16",
                      "svdq_check_device", "svdq_check_arch", "svdq_act_packed_bytes",
                      "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed", "svdq_pack_act",
-                     "svdq_prepack_weight", "svdq_gemm_w4a4_packed"):
+                     "svdq_prepack_weight", "svdq_gemm_w4a4_packed", "svdq_prepacked_l1_bytes",
+                     "svdq_prepack_l1"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -228,9 +228,31 @@ svdq_status svdq_prepacked_weight_bytes(const svdq_layer_cfg* cfg, int64_t* byte
     return SVDQ_OK;
 }
 
+svdq_status svdq_prepacked_l1_bytes(const svdq_layer_cfg* cfg, int64_t* bytes) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    if (bytes == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = svdq::prepacked_l1_bytes(cfg->rank, cfg->in_features);
+    return SVDQ_OK;
+}
+
+svdq_status svdq_prepack_l1(const svdq_layer_cfg* cfg, const void* l1, void* l1_packed,
+                            svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    if (cfg->rank == 0) return SVDQ_OK;
+    SVDQ_TRY(check_ptr(l1, "l1", 16));
+    SVDQ_TRY(check_ptr(l1_packed, "l1_packed", 16));
+    SVDQ_TRY(check_current_device());
+    svdq::launch_prepack_l1(cfg->rank, cfg->in_features, l1, l1_packed,
+                            reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_prepack_l1");
+}
+
 svdq_status svdq_quantize_act_packed(const svdq_layer_cfg* cfg, int64_t M, const void* x,
-                                     const float* smooth_inv, const void* l1, void* act_packed,
-                                     float* act_scales, void* lora_act, svdq_stream_t stream) {
+                                     const float* smooth_inv, const void* l1_packed,
+                                     void* act_packed, float* act_scales, void* lora_act,
+                                     svdq_stream_t stream) {
     SVDQ_TRY(check_cfg(cfg));
     SVDQ_TRY(check_int4(cfg));
     if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
@@ -240,14 +262,14 @@ svdq_status svdq_quantize_act_packed(const svdq_layer_cfg* cfg, int64_t M, const
     if (act_scales != nullptr && !aligned(act_scales, 4))
         return fail(SVDQ_ERR_INVALID_ARG, "act_scales is not 4-byte aligned");
     if (cfg->rank > 0) {
-        SVDQ_TRY(check_ptr(l1, "l1", 16));
+        SVDQ_TRY(check_ptr(l1_packed, "l1_packed", 16));
         SVDQ_TRY(check_ptr(lora_act, "lora_act", 16));
     }
     if (M > (int64_t)1 << 35)
         return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
     SVDQ_TRY(check_current_device());
     if (M == 0) return SVDQ_OK;
-    svdq::QuantArgs a{M, cfg->in_features, cfg->rank, 1, x, smooth_inv, l1, 1.0f, act_packed,
+    svdq::QuantArgs a{M, cfg->in_features, cfg->rank, 1, x, smooth_inv, l1_packed, 1.0f, act_packed,
                       act_scales, lora_act};
     svdq::launch_quantize_act(a, reinterpret_cast<hipStream_t>(stream));
     return after_launch("svdq_quantize_act_packed");

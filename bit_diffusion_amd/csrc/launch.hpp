@@ -12,7 +12,7 @@ struct QuantArgs {
     int mode;       // 0 INT4 nibbles, 1 INT4 packed (packed_layout.hpp), 2 NVFP4 nibbles
     const void* x;
     const float* smooth_inv;
-    const void* l1;
+    const void* l1;   // [r, K] row-major; prepacked (launch_prepack_l1) in mode 1
     float S;
     void* codes;    // nibbles, or the packed activation buffer in mode 1
     void* scales;   // may be NULL in mode 1
@@ -70,6 +70,8 @@ void launch_awq_gemv(const AwqArgs& a, hipStream_t st);
 
 void launch_prepack_wgt(int N, int K, const void* wcodes, const void* wscales, void* out,
                         hipStream_t st);
+int64_t prepacked_l1_bytes(int r, int K);
+void launch_prepack_l1(int r, int K, const void* l1, void* out, hipStream_t st);
 void launch_pack_act(int64_t M, int K, const void* acodes, const void* ascales, void* out,
                      hipStream_t st);
 bool gemm_w4a4_fp6_init();

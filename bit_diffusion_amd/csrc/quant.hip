@@ -17,7 +17,9 @@
 // single v_cvt_scalef32_2xpk16_fp6_f32.  The group absmax is a max over the lane's 32
 // values and its partner lane l ^ 16.  For the low-rank down-projection the same registers
 // are the A operands of four v_mfma_f32_16x16x32_bf16 per 16 ranks (the MFMA contracts any
-// consistent permutation of the channels; L1 is loaded in the matching order).
+// consistent permutation of the channels; L1 is loaded in the matching order).  The packed
+// mode reads L1 prepacked in that lane order (prepack_l1_kernel below), one contiguous 1 KiB
+// per operand and wave; the nibble modes read the row-major [r, K] factor, 16 rows a load.
 //
 // A wave issues the loads of up to kAhead steps at once, in straight-line code, so every
 // step waits only for its own data.  smooth_inv goes through a wave-private LDS slice (one
@@ -60,25 +62,38 @@ struct Stage {
     uint4 l1[kPrefetchL1<RB> && RB > 0 ? 4 * RB : 1];    // L1 row (16 b + l % 16), same channels
 };
 
-__device__ __forceinline__ uint4 load_l1(const uint16_t* l1r, int K, int b, int k0, int t) {
-    return *reinterpret_cast<const uint4*>(l1r + (int64_t)b * 16 * K + k0 + 8 * t);
+// Where the lane's L1 operands live.  Row-major [r, K]: row 16 b + l % 16 (`base` points at
+// row l % 16), channels k0 + 8 t.  Prepacked: unit (c, b, t), lane l (`base` points at the
+// lane's 16 bytes of unit 0).
+template <int MODE>
+struct L1Src {
+    const uint16_t* base;
+    int K;
+};
+
+template <int MODE, int RB>
+__device__ __forceinline__ uint4 load_l1(const L1Src<MODE>& s, int c, int b, int k0, int t) {
+    if constexpr (MODE == kInt4Packed)
+        return *reinterpret_cast<const uint4*>(s.base + (((int64_t)c * RB + b) * 4 + t) * 512);
+    else
+        return *reinterpret_cast<const uint4*>(s.base + (int64_t)b * 16 * s.K + k0 + 8 * t);
 }
 
-template <int RB>
-__device__ __forceinline__ void load_stage_l1(Stage<RB>& st, const uint16_t* l1r, int K, int k0) {
+template <int MODE, int RB>
+__device__ __forceinline__ void load_stage_l1(Stage<RB>& st, const L1Src<MODE>& l1s, int c, int k0) {
     if constexpr (kPrefetchL1<RB>)
 #pragma unroll
         for (int b = 0; b < RB; ++b)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) st.l1[4 * b + t] = load_l1(l1r, K, b, k0, t);
+            for (int t = 0; t < 4; ++t) st.l1[4 * b + t] = load_l1<MODE, RB>(l1s, c, b, k0, t);
 }
 
-template <int RB>
-__device__ __forceinline__ void load_stage(Stage<RB>& st, const uint16_t* xr, const uint16_t* l1r,
-                                           int K, int k0, bool with_l1) {
+template <int MODE, int RB>
+__device__ __forceinline__ void load_stage(Stage<RB>& st, const uint16_t* xr, const L1Src<MODE>& l1s,
+                                           int c, int k0, bool with_l1) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) st.x[t] = *reinterpret_cast<const uint4*>(xr + k0 + 8 * t);
-    if (with_l1) load_stage_l1<RB>(st, l1r, K, k0);
+    if (with_l1) load_stage_l1<MODE, RB>(st, l1s, c, k0);
 }
 
 // The lane's 32 values in the order of the FP6 conversion: ev[i] is channel 2i (the low
@@ -304,7 +319,7 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
     const int64_t row = m0 + rl;
     const bool row_ok = row < M;
     const uint16_t* xr = (const uint16_t*)p.x + (row_ok ? row : M - 1) * (int64_t)K;
-    const uint16_t* l1r = (const uint16_t*)p.l1 + (int64_t)rl * K;
+    const L1Src<MODE> l1s{(const uint16_t*)p.l1 + (MODE == kInt4Packed ? 8 * lane : (int64_t)rl * K), K};
     const int nc = (G + 1) >> 1;                                       // steps over K
     const int nsw = nc > wave ? (nc - wave + kQWaves - 1) / kQWaves : 0;  // this wave's steps
     f32x4 acc[RB > 0 ? RB : 1];
@@ -323,8 +338,8 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
 #pragma unroll
         for (int s = 0; s < NA; ++s) {
             const int c = wave + kQWaves * min(it0 + s, nsw - 1);
-            load_stage<RB>(st[s], xr, l1r, K, min(c * kStep + 32 * q4, K - 32),
-                           !(kLateL1<RB> && s == NA - 1));
+            load_stage<MODE, RB>(st[s], xr, l1s, c, min(c * kStep + 32 * q4, K - 32),
+                                 !(kLateL1<RB> && s == NA - 1));
         }
 #pragma unroll
         for (int s = 0; s < NA; ++s) *reinterpret_cast<uint2*>(&si_lds[wave][s][2 * lane]) = siv[s];
@@ -349,7 +364,7 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
                         for (int t = 0; t < 4; ++t) {
                             uint4 w;
                             if constexpr (kPrefetchL1<RB>) w = st[s].l1[4 * b + t];
-                            else w = load_l1(l1r, K, b, k0, t);
+                            else w = load_l1<MODE, RB>(l1s, c, b, k0, t);
                             acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                 as_bf16x8(st[s].x[t]), as_bf16x8(w), acc[b], 0, 0, 0);
                         }
@@ -357,11 +372,32 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
             }
             if (kLateL1<RB> && s == 0) {   // the last stage's L1 slice, into stage 0's registers
                 const int c = wave + kQWaves * min(it0 + NA - 1, nsw - 1);
-                load_stage_l1<RB>(st[NA - 1], l1r, K, min(c * kStep + 32 * q4, K - 32));
+                load_stage_l1<MODE, RB>(st[NA - 1], l1s, c, min(c * kStep + 32 * q4, K - 32));
             }
         }
     }
     lowrank_finish<RB>(acc, red, m0, M, (uint16_t*)p.lora);
+}
+
+// Prepacked L1: the low-rank factor [r, K] (bf16) in the lane order of the B operands of
+// the packed mode's v_mfma_f32_16x16x32_bf16, so every operand load is one contiguous 1 KiB
+// per wave.  Unit (c, b, t) = 128-channel step c, rank block b (ranks 16 b .. 16 b + 15),
+// slice t (0..3); lane L of a unit holds the 8 bf16 L1[16 b + L % 16][128 c + 32 (L / 16) +
+// 8 t + j], j = 0..7, at byte 16 L.  Units are stored in the order [c][b][t]; channels at or
+// beyond K (the second half of the last step when K / 64 is odd) hold zeros.  One thread
+// per 16-byte lane of a unit.
+__global__ __launch_bounds__(256) void prepack_l1_kernel(int RB, int K, int64_t units,
+                                                         const uint16_t* __restrict__ l1,
+                                                         uint4* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= units) return;
+    const int L = (int)(i & 63), t = (int)((i >> 6) & 3);
+    const int64_t cb = i >> 8;
+    const int b = (int)(cb % RB);
+    const int64_t c = cb / RB;
+    const int64_t k = c * kStep + 32 * (L >> 4) + 8 * t;
+    const int n = 16 * b + (L & 15);
+    out[i] = k < K ? *reinterpret_cast<const uint4*>(l1 + (int64_t)n * K + k) : make_uint4(0u, 0u, 0u, 0u);
 }
 
 template <int RB, int MODE>
@@ -384,6 +420,16 @@ void launch_rb(const QuantArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int64_t prepacked_l1_bytes(int r, int K) {
+    return (int64_t)((K + kStep - 1) / kStep) * kStep * r * 2;
+}
+
+void launch_prepack_l1(int r, int K, const void* l1, void* out, hipStream_t st) {
+    const int64_t units = prepacked_l1_bytes(r, K) / 16;
+    hipLaunchKernelGGL(prepack_l1_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st,
+                       r / 16, K, units, (const uint16_t*)l1, (uint4*)out);
+}
 
 void launch_quantize_act(const QuantArgs& a, hipStream_t st) {
     switch (a.r / 16) {

@@ -161,9 +161,17 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
  *
  * svdq_act_packed_bytes / svdq_prepacked_weight_bytes: buffer sizes for `cfg` (INT4 only)
  *   and M rows.
+ * svdq_prepacked_l1_bytes: buffer size of the prepacked low-rank factor for `cfg`
+ *   (ceil(K / 128) * 128 * rank * 2 bytes; 0 at rank 0).
+ * svdq_prepack_l1: the low-rank down-projection factor l1 bf16 [rank, K] row-major ->
+ *   l1_packed, reordered so the activation kernel reads each of its MFMA operands as one
+ *   contiguous 1 KiB (a layout detail of this library; the values are l1's, channels past
+ *   K are zero).  Once per layer, like the weight prepack.  A no-op at rank 0.
  * svdq_quantize_act_packed: as svdq_quantize_act (INT4), writing the codes into act_packed
- *   instead of nibbles; the codes, the fp32 scales (act_scales, may be NULL) and lora_act
- *   are bit-identical to svdq_quantize_act's.  Padding rows of act_packed are zero.
+ *   instead of nibbles and taking the low-rank factor as l1_packed (svdq_prepack_l1
+ *   output; may be NULL at rank 0); the codes, the fp32 scales (act_scales, may be NULL)
+ *   and lora_act are bit-identical to svdq_quantize_act's on the unpacked l1.  Padding rows
+ *   of act_packed are zero.
  * svdq_pack_act: act_codes [M, K/2] nibbles + act_scales [M, K/64] fp32 (svdq_quantize_act
  *   output) -> act_packed.
  * svdq_prepack_weight: wgt_codes [N, K/2] nibbles (full range [-8, 7]) + wgt_scales
@@ -175,9 +183,13 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
  */
 svdq_status svdq_act_packed_bytes(const svdq_layer_cfg* cfg, int64_t M, int64_t* bytes);
 svdq_status svdq_prepacked_weight_bytes(const svdq_layer_cfg* cfg, int64_t* bytes);
+svdq_status svdq_prepacked_l1_bytes(const svdq_layer_cfg* cfg, int64_t* bytes);
+svdq_status svdq_prepack_l1(const svdq_layer_cfg* cfg, const void* l1, void* l1_packed,
+                            svdq_stream_t stream);
 svdq_status svdq_quantize_act_packed(const svdq_layer_cfg* cfg, int64_t M, const void* x,
-                                     const float* smooth_inv, const void* l1, void* act_packed,
-                                     float* act_scales, void* lora_act, svdq_stream_t stream);
+                                     const float* smooth_inv, const void* l1_packed,
+                                     void* act_packed, float* act_scales, void* lora_act,
+                                     svdq_stream_t stream);
 svdq_status svdq_pack_act(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
                           const float* act_scales, void* act_packed, svdq_stream_t stream);
 svdq_status svdq_prepack_weight(const svdq_layer_cfg* cfg, const void* wgt_codes,

@@ -98,9 +98,18 @@ def quantize_packed(x_bf16, smooth_inv, l1=None, N=1, with_scales=True):
     scales = empty((M, K // 64), np.float32) if with_scales else None
     lora = empty((M, r), np.uint16) if r else None
     si = smooth_inv if torch.is_tensor(smooth_inv) else dev(np.asarray(smooth_inv, np.float32))
-    l1d = None if l1 is None else (l1 if torch.is_tensor(l1) else dev(l1))
-    bd.svdq_quantize_act_packed(cfg, M, x, si, l1d, buf, scales, lora)
+    l1p = None if l1 is None else prepack_l1(l1, K)
+    bd.svdq_quantize_act_packed(cfg, M, x, si, l1p, buf, scales, lora)
     return buf, scales, lora
+
+
+def prepack_l1(l1, K):
+    """svdq_prepack_l1: bf16 bits [r, K] -> the prepacked low-rank factor."""
+    l1d = l1 if torch.is_tensor(l1) else dev(l1)
+    cfg = bd.LayerCfg.make(K, 1, l1d.shape[0])
+    out = torch.empty(bd.svdq_prepacked_l1_bytes(cfg), dtype=torch.uint8, device="cuda:0")
+    bd.svdq_prepack_l1(cfg, l1d, out)
+    return out
 
 
 def gemm_packed(apacked, wpacked, M, K, N, lora=None, l2=None, bias=None, act=0, out_bf16=False):

@@ -116,6 +116,23 @@ def test_awq_rejects_bad_args():
     assert call(M=-1) == bd.SVDQ_ERR_INVALID_ARG
 
 
+def test_prepacked_l1_size_and_bad_args():
+    # ceil(K / 128) 128-channel steps x rank x 2 bytes; K / 64 odd rounds up by one group
+    assert bd.svdq_prepacked_l1_bytes(bd.LayerCfg.make(3072, 3072, 32)) == 3072 * 32 * 2
+    assert bd.svdq_prepacked_l1_bytes(bd.LayerCfg.make(192, 64, 16)) == 256 * 16 * 2
+    assert bd.svdq_prepacked_l1_bytes(bd.LayerCfg.make(512, 64, 0)) == 0
+    L = bd.lib()
+    cfg = bd.LayerCfg.make(512, 512, 16)
+    assert L.svdq_prepack_l1(ctypes.byref(cfg), None, FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_prepack_l1(ctypes.byref(cfg), FAKE, FAKE + 4, None) == bd.SVDQ_ERR_INVALID_ARG
+    nv = bd.LayerCfg.make(512, 512, 16, "nvfp4")
+    assert L.svdq_prepack_l1(ctypes.byref(nv), FAKE, FAKE, None) != bd.SVDQ_OK
+    # the packed activation kernel needs the prepacked factor whenever the rank is non-zero
+    assert L.svdq_quantize_act_packed(ctypes.byref(cfg), 16, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                      None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "l1_packed" in bd.svdq_last_error()
+
+
 def test_python_binding_raises_with_message():
     cfg = bd.LayerCfg.make(100, 512, 16)
     with pytest.raises(bd.SvdqError) as e:

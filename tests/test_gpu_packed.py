@@ -7,6 +7,7 @@ CPU oracle.
   types.  Bar: relative Frobenius error <= 1e-3 of the oracle's fp64 result (fp32 output);
   bf16 output within one bf16 ulp (plus 2^-16 of the largest magnitude), >= 99% equal to
   the oracle rounded to bf16.
+* svdq_prepack_l1: the reordered low-rank factor against the layout written out on the host.
 * svdq_quantize_act_packed: the codes read back from the packed buffer, the fp32 scales and
   lora_act equal svdq_quantize_act's and the oracle's bit for bit (lora_act within its fp32
   bound); the scale words are the bf16 hi/lo split of the scales; padding rows are zero.
@@ -116,6 +117,26 @@ def test_quantize_packed_bit_exact(M, K, r):
         gu.assert_lora_close(gu.host(lora), ol, x, l1)
     # the packed buffer from nibbles is the same bytes
     assert torch.equal(gu.pack_act(codes_n, scales_n, K), buf)
+
+
+@pytest.mark.parametrize("K,r", [(64, 16), (192, 32), (3072, 32), (320, 128)])
+def test_prepack_l1_layout(K, r):
+    """svdq_prepack_l1 against the layout written out on the host: unit (c, b, t), lane L
+    holds L1[16 b + L % 16][128 c + 32 (L / 16) + 8 t .. + 8], zeros past K."""
+    rng = np.random.default_rng(910 + K + r)
+    l1 = synth.random_bf16(rng, (r, K), 0.05)
+    got = gu.host(gu.prepack_l1(l1, K)).view(np.uint16)
+    nc = (K + 127) // 128
+    padded = np.zeros((r, nc * 128), np.uint16)
+    padded[:, :K] = l1
+    want = np.empty((nc, r // 16, 4, 64, 8), np.uint16)
+    for c in range(nc):
+        for b in range(r // 16):
+            for t in range(4):
+                for L in range(64):
+                    k = 128 * c + 32 * (L // 16) + 8 * t
+                    want[c, b, t, L] = padded[16 * b + L % 16, k:k + 8]
+    assert np.array_equal(got, want.reshape(-1))
 
 
 def test_quantize_packed_without_scales():
