@@ -193,12 +193,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         return cg < kAChunks ? a_base + (int64_t)h * kAStage + cg * 1024
                              : b_base + (int64_t)h * kBStage + (cg - kAChunks) * 1024;
     };
-    const uint64_t mask_lo4 = (wave < 4) ? ~0ull : 0ull;
+    const uint64_t mask_lo4 = uniform_u64((wave < 4) ? ~0ull : 0ull);
+    // Source of copy j for third 0 and its advance per third, both wave-uniform (SGPRs):
+    // chunk c = wave + 8 j is an activation or a weight chunk depending on the wave only
+    // (c is clamped for the masked seventh copy of waves 4-7, which reads nothing).
+    uint64_t src0[7];
+    uint32_t step[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+        const int c = min(wave + 8 * j, 51);
+        const int cg = c >= 26 ? c - 26 : c;
+        src0[j] = uniform_u64((uint64_t)chunk_src(0, c));
+        step[j] = __builtin_amdgcn_readfirstlane(cg < kAChunks ? 2 * kAStage : 2 * kBStage);
+    }
     auto issue_j = [&](int t, int j) {   // groups 2t and 2t + 1 both exist
         const int c = wave + 8 * j;
         const uint32_t dst = lds0 + (t % 3) * (2 * kStageBytes) + c * 1024;
-        if (j < 6) dma_chunk(chunk_src(2 * t, c), voff, dst);
-        else dma_chunk_m(chunk_src(2 * t, c), voff, dst, mask_lo4);
+        const uint8_t* src = (const uint8_t*)(src0[j] + (uint64_t)((uint32_t)t * step[j]));
+        if (j < 6) dma_chunk(src, voff, dst);
+        else dma_chunk_m(src, voff, dst, mask_lo4);
     };
     for (int h = 0; h < min(G, 4); ++h) issue(h, h);
 
@@ -245,7 +258,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         for (int i = 0; i < 2; ++i) {
             const uint8_t* Ab = S + (2 * wm + i) * kABlock;
             const uint4 v0 = *reinterpret_cast<const uint4*>(Ab + lane * 16);
-            const uint2 v1 = *reinterpret_cast<const uint2*>(Ab + 1024 + lane * 8);
+            // volatile: a load of its own, straight into the operand's registers (merged
+            // with its neighbour it would need two moves)
+            const uint64_t v1q = *(const volatile __attribute__((address_space(3))) uint64_t*)(Ab + 1024 + lane * 8);
+            const uint2 v1 = make_uint2((uint32_t)v1q, (uint32_t)(v1q >> 32));
             const uint2 x = *reinterpret_cast<const uint2*>(Ab + kFrag + fr * 8);
             f.a[i].s0123 = i32x4{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w};
             f.a[i].s45 = (__attribute__((ext_vector_type(2))) int){(int)v1.x, (int)v1.y};
@@ -257,7 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         for (int j = 0; j < 3; ++j) {
             const uint8_t* Bb = S + kAStage + (3 * wn + j) * kBBlock;
             const uint4 w0v = *reinterpret_cast<const uint4*>(Bb + lane * 16);
-            const uint2 w1v = *reinterpret_cast<const uint2*>(Bb + 1024 + lane * 8);
+            const uint64_t w1q = *(const volatile __attribute__((address_space(3))) uint64_t*)(Bb + 1024 + lane * 8);
+            const uint2 w1v = make_uint2((uint32_t)w1q, (uint32_t)(w1q >> 32));
             f.w[j].s0123 = i32x4{(int)w0v.x, (int)w0v.y, (int)w0v.z, (int)w0v.w};
             f.w[j].s45 = (__attribute__((ext_vector_type(2))) int){(int)w1v.x, (int)w1v.y};
             f.wp[j] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(Bb + kFrag + lane * 8));
@@ -265,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     };
     // Software-pipelined: the two MFMAs of pair q+1 are issued around the fmas of pair q,
     // so the MFMA pipe and the VALU work at the same time within one wave.
-    auto compute = [&](const Frags& f) {
+    auto compute = [&](const Frags& f, auto&& mid) {
         f32x16 r0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[0], f.w[0], f32x16{}, 2, 2, 0, 127, 0, 127);
         f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(f.ap[0], f.wp[0], f32x16{}, 0, 0, 0);
 #pragma unroll
@@ -288,6 +305,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
 #pragma unroll
             for (int e = 8; e < 16; ++e) acc[i][j][e] = fmaf(r0[e], p0[e], acc[i][j][e]);
             __builtin_amdgcn_sched_barrier(0);
+            if (q == 3) {   // the second column's weight operands are no longer read
+                mid();
+                __builtin_amdgcn_sched_barrier(0);
+            }
             r0 = r1;
             p0 = p1;
         }
@@ -299,17 +320,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         barrier();      // every wave's have; third t-1's buffer is no longer read
         const uint8_t* S = smem + (t % 3) * (2 * kStageBytes);
         {
-            Frags f;
+            Frags f, f1;
             load_frags(S, f);
-            compute(f);
+            // the second group's operands are read while the first one's last column computes
+            compute(f, [&] { load_frags(S + kStageBytes, f1); });
             __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) issue_j(t + 2, j);   // third t+2's copies, spread over the third
-        {
-            Frags f;
-            load_frags(S + kStageBytes, f);
-            compute(f);
+            for (int j = 0; j < 3; ++j) issue_j(t + 2, j);   // third t+2's copies, spread over the third
+            compute(f1, [] {});
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -322,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     for (int g = 2 * t; g < min(G, 2 * t + 2); ++g) {
         Frags f;
         load_frags(smem + (g % kStages) * kStageBytes, f);
-        compute(f);
+        compute(f, [] {});
     }
     if (2 * t + 2 < G) {
         wait_vm<0>();
@@ -330,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         for (int g = 2 * t + 2; g < G; ++g) {
             Frags f;
             load_frags(smem + (g % kStages) * kStageBytes, f);
-            compute(f);
+            compute(f, [] {});
         }
     }
 
