@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     };
     // Software-pipelined: the two MFMAs of pair q+1 are issued around the fmas of pair q,
     // so the MFMA pipe and the VALU work at the same time within one wave.
-    auto compute = [&](const Frags& f, auto&& mid) {
+    auto compute = [&](const Frags& f) {
         f32x16 r0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[0], f.w[0], f32x16{}, 2, 2, 0, 127, 0, 127);
         f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(f.ap[0], f.wp[0], f32x16{}, 0, 0, 0);
 #pragma unroll
@@ -305,8 +305,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
 #pragma unroll
             for (int e = 8; e < 16; ++e) acc[i][j][e] = fmaf(r0[e], p0[e], acc[i][j][e]);
             __builtin_amdgcn_sched_barrier(0);
-            if (q == 3) {   // the second column's weight operands are no longer read
-                mid();
+            r0 = r1;
+            p0 = p1;
+        }
+    };
+
+    // Both groups of a third in one software pipeline of twelve 32x32 sub-tiles (no drain
+    // and refill between the groups): the second group's operands are read once the first
+    // group's first two columns are issued, `between` runs after the first group's FMAs
+    // have started the second group's MFMAs.
+    auto compute2 = [&](const Frags& fa, Frags& fb, const uint8_t* Sb, auto&& between) {
+        f32x16 r0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa.a[0], fa.w[0], f32x16{}, 2, 2, 0, 127, 0, 127);
+        f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fa.ap[0], fa.wp[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 12; ++q) {
+            const int i = q & 1, j = (q >> 1) % 3;
+            const int q1 = q + 1, i1 = q1 & 1, j1 = (q1 >> 1) % 3;
+            const Frags& fn = q1 < 6 ? fa : fb;
+            f32x16 r1, p1;
+            if (q < 11)
+                r1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fn.a[i1], fn.w[j1], f32x16{}, 2, 2, 0, 127, 0, 127);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i][j][e] = fmaf(r0[e], p0[e], acc[i][j][e]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q < 11) p1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fn.ap[i1], fn.wp[j1], f32x16{}, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 8; e < 16; ++e) acc[i][j][e] = fmaf(r0[e], p0[e], acc[i][j][e]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == 3) {   // the first group's weight columns 0 and 1 are no longer read
+                load_frags(Sb, fb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (q == 5) {
+                between();
                 __builtin_amdgcn_sched_barrier(0);
             }
             r0 = r1;
@@ -322,12 +355,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         {
             Frags f, f1;
             load_frags(S, f);
-            // the second group's operands are read while the first one's last column computes
-            compute(f, [&] { load_frags(S + kStageBytes, f1); });
-            __builtin_amdgcn_sched_barrier(0);
+            compute2(f, f1, S + kStageBytes, [&] {
 #pragma unroll
-            for (int j = 0; j < 3; ++j) issue_j(t + 2, j);   // third t+2's copies, spread over the third
-            compute(f1, [] {});
+                for (int j = 0; j < 3; ++j) issue_j(t + 2, j);   // third t+2's copies, spread over the third
+            });
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -340,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     for (int g = 2 * t; g < min(G, 2 * t + 2); ++g) {
         Frags f;
         load_frags(smem + (g % kStages) * kStageBytes, f);
-        compute(f, [] {});
+        compute(f);
     }
     if (2 * t + 2 < G) {
         wait_vm<0>();
@@ -348,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         for (int g = 2 * t + 2; g < G; ++g) {
             Frags f;
             load_frags(smem + (g % kStages) * kStageBytes, f);
-            compute(f, [] {});
+            compute(f);
         }
     }
 
