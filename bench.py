@@ -20,7 +20,8 @@ avoids not counted), with every input already in HBM.  Inputs rotate through eno
 256 MB last-level cache.  Unless --only-main, the line also carries the secondary paths:
 the AWQ W4A16 GEMV of the adaLN modulation (M=2, K=3072, N=18432; GB/s against HBM) and the
 NVFP4 fused-QKV linear (M=4096, K=3072, N=9216, rank 32; TOPS against the bf16 and FP4
-peaks).  `roofline.traffic` comes from the HBM byte counters recorded for the GEMM kernel
+peaks), and the MLP block (M=4608, 3072 -> 12288 -> 3072, fc1 with GELU and bf16 output
+feeding fc2's activation kernel; TOPS).  `roofline.traffic` comes from the HBM byte counters recorded for the GEMM kernel
 (profiles/), and is null when the kernel's sources changed since they were taken.
 """
 import argparse
@@ -191,6 +192,77 @@ def nvfp4_leg(steps, sp, stream):
     return {"workload": "nvfp4_qkv_4096x3072x9216_r32", "ms_per_linear": round(ms, 4),
             "TOPS": round(tops, 2), "bf16_peak_frac": round(tops / BF16_PEAK_TFLOPS, 4),
             "fp4_peak_frac": round(tops / FP4_PEAK_TFLOPS, 4)}
+
+
+def mlp_leg(steps, sp, stream):
+    """DiT MLP block on the packed path (M=4608 tokens, 3072 -> 12288 -> 3072, rank 32):
+    fc1 with GELU(tanh) in its epilogue writing bf16, then fc2's activation kernel reads that
+    output and fc2 writes fp32.  Weights are this library's own quantization of bf16
+    N(0, 0.02) draws; activations bf16 N(0, 1) with 31 outlier channels x50."""
+    import torch
+    import bit_diffusion_amd as bd
+    Mm, K1, N1, Rm = 4608, 3072, 12288, 32
+    K2, N2 = N1, K1
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(31)
+
+    def bf16(shape, std):
+        return (torch.randn(shape, device=dev, generator=g) * std).to(torch.bfloat16).view(torch.int16)
+
+    def layer(K, N):
+        cfg = bd.LayerCfg.make(K, N, Rm)
+        cw = bd.LayerCfg.make(K, N, 0)
+        w = bf16((N, K), 0.02)
+        ones = torch.ones(K, dtype=torch.float32, device=dev)
+        wc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        ws = torch.empty((N, K // 64), dtype=torch.float32, device=dev)
+        bd.svdq_quantize_act(cw, N, w, ones, None, 1.0, wc, ws, None)
+        packed = torch.empty(bd.svdq_prepacked_weight_bytes(cw), dtype=torch.uint8, device=dev)
+        bd.svdq_prepack_weight(cw, wc, ws, packed)
+        l1p = torch.empty(bd.svdq_prepacked_l1_bytes(cfg), dtype=torch.uint8, device=dev)
+        bd.svdq_prepack_l1(cfg, bf16((Rm, K), 0.02), l1p)
+        return dict(cfg=cfg, packed=packed, l1p=l1p, l2=bf16((N, Rm), 0.02), bias=bf16((N,), 0.02),
+                    si=torch.rand(K, device=dev, generator=g) + 0.5,
+                    apk=torch.empty(bd.svdq_act_packed_bytes(cfg, Mm), dtype=torch.uint8, device=dev),
+                    lora=torch.empty((Mm, Rm), dtype=torch.int16, device=dev))
+
+    fc1, fc2 = layer(K1, N1), layer(K2, N2)
+    x = bf16((Mm, K1), 1.0)
+    x.view(torch.bfloat16)[:, torch.randperm(K1, device=dev, generator=g)[:31]] *= 50
+    h = torch.empty((Mm, N1), dtype=torch.int16, device=dev)
+    y = torch.empty((Mm, N2), dtype=torch.float32, device=dev)
+
+    def quant(L, a):
+        bd.svdq_quantize_act_packed(L["cfg"], Mm, a, L["si"], L["l1p"], L["apk"], None, L["lora"], sp)
+
+    def gemm(L, act, dt, out):
+        bd.svdq_gemm_w4a4_packed(L["cfg"], Mm, L["apk"], L["packed"], L["lora"], L["l2"], L["bias"],
+                                 act, dt, out, sp)
+
+    def go(i):
+        quant(fc1, x)
+        gemm(fc1, bd.SVDQ_ACT_GELU_TANH, bd.SVDQ_DT_BF16, h)
+        quant(fc2, h)
+        gemm(fc2, bd.SVDQ_ACT_NONE, bd.SVDQ_DT_F32, y)
+
+    go(0)
+    torch.cuda.synchronize()
+    n = max(3, steps // 5)
+    ms = time_launches(go, n, stream)
+    ms_fc1 = time_launches(lambda i: gemm(fc1, bd.SVDQ_ACT_GELU_TANH, bd.SVDQ_DT_BF16, h), n, stream)
+    ms_q2 = time_launches(lambda i: quant(fc2, h), n, stream)
+    ops1 = 2.0 * Mm * N1 * K1 + 2.0 * Mm * N1 * Rm
+    ops2 = 2.0 * Mm * N2 * K2 + 2.0 * Mm * N2 * Rm
+    ops = ops1 + ops2 + 2.0 * Mm * (K1 + K2) * Rm
+    tops = ops / (ms * 1e-3) / 1e12
+    q2_bytes = Mm * K2 * 2 + bd.svdq_act_packed_bytes(fc2["cfg"], Mm) + Mm * Rm * 2 + Rm * K2 * 2
+    return {"workload": "mlp_4608x3072x12288x3072_r32", "ms_per_mlp": round(ms, 4),
+            "TOPS": round(tops, 2), "pct_of_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+            "fc1_gelu_bf16_gemm_ms": round(ms_fc1, 4),
+            "fc1_gelu_bf16_gemm_TOPS": round(ops1 / (ms_fc1 * 1e-3) / 1e12, 2),
+            "fc2_quantize_ms": round(ms_q2, 4),
+            "fc2_quantize_GBs": round(q2_bytes / (ms_q2 * 1e-3) / 1e9, 1)}
 
 
 def make_inputs(copies):
@@ -394,6 +466,7 @@ def main():
     if not args.only_main:
         out["awq"] = awq_leg(args.steps, sp, stream)
         out["nvfp4"] = nvfp4_leg(args.steps, sp, stream)
+        out["mlp"] = mlp_leg(args.steps, sp, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     print(json.dumps(out), flush=True)
