@@ -97,10 +97,8 @@ __device__ __forceinline__ void dma_chunk_m(const uint8_t* sbase, uint32_t voff,
                  : "=&s"(saved) : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(uniform_u64(mask)), "s"(uniform_ptr(sbase)) : "memory", "scc");
 }
 
-__device__ __forceinline__ void tile_coords(int& pid_m, int& pid_n, int num_m, int num_n) {
-    const int nt = num_m * num_n;
-    int t = blockIdx.x;
-    if ((nt & 7) == 0) t = (t & 7) * (nt >> 3) + (t >> 3);   // contiguous tile range per XCD
+// Output tile t (row-major over groups of four tile rows) -> tile coordinates.
+__device__ __forceinline__ void tile_of(int t, int& pid_m, int& pid_n, int num_m, int num_n) {
     const int GM = 4;
     const int group = GM * num_n;
     const int first_m = (t / group) * GM;
@@ -108,6 +106,25 @@ __device__ __forceinline__ void tile_coords(int& pid_m, int& pid_n, int num_m, i
     const int r = t % group;
     pid_m = first_m + r % gm;
     pid_n = r / gm;
+}
+
+// Workgroup -> (tile, K split).  Consecutive workgroups go to different XCDs, so block b is
+// remapped to give each XCD a contiguous range of tiles.  With a K split (p.nsplit > 1),
+// blocks from p.nfull on take the remaining tiles t >= p.nfull in p.nsplit parts of
+// p.gsplit groups each.
+__device__ __forceinline__ void work_of(const PackedGemmArgs& p, int num_m, int num_n, int& pid_m,
+                                        int& pid_n, int& split) {
+    const int nt = num_m * num_n;
+    int b = blockIdx.x, t;
+    split = -1;
+    if (p.nsplit > 1 && b >= p.nfull) {
+        t = p.nfull + (b - p.nfull) / p.nsplit;
+        split = (b - p.nfull) % p.nsplit;
+    } else {
+        const int n = p.nsplit > 1 ? p.nfull : nt;
+        t = (n & 7) == 0 ? (b & 7) * (n >> 3) + (b >> 3) : b;
+    }
+    tile_of(t, pid_m, pid_n, num_m, num_n);
 }
 
 // Epilogue staging: each wave writes its 32 x 96 half-tiles to LDS and stores whole
@@ -123,15 +140,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = p.M;
-    const int N = p.N, G = p.K >> 6;
+    const int N = p.N, Gall = p.K >> 6;
     const int num_m = (int)((M + kBM - 1) / kBM), num_n = (N + kBN - 1) / kBN;
-    int pid_m, pid_n;
-    tile_coords(pid_m, pid_n, num_m, num_n);
+    int pid_m, pid_n, split;
+    work_of(p, num_m, num_n, pid_m, pid_n, split);
     const int64_t m0 = (int64_t)pid_m * kBM;
     const int n0 = pid_n * kBN;
+    // this workgroup's groups: all, or split `split` of a K-split tile
+    const int g_begin = split < 0 ? 0 : split * p.gsplit;
+    const int G = split < 0 ? Gall : min(Gall - g_begin, p.gsplit);
 
-    const uint8_t* a_base = (const uint8_t*)p.act + (int64_t)pid_m * G * kAStage;
-    const uint8_t* b_base = (const uint8_t*)p.wgt + (int64_t)pid_n * G * kBStage;
+    const uint8_t* a_base = (const uint8_t*)p.act + ((int64_t)pid_m * Gall + g_begin) * kAStage;
+    const uint8_t* b_base = (const uint8_t*)p.wgt + ((int64_t)pid_n * Gall + g_begin) * kBStage;
     const uint32_t lds0 = lds_offset(smem);
     const uint32_t voff = lane * 16;
 
@@ -158,7 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     // the wait for the first buffers instead of standing in the epilogue.
     const uint16_t* lora = (const uint16_t*)p.lora;
     const uint16_t* l2 = (const uint16_t*)p.l2;
-    const int r = p.r;
+    const int r = split > 0 ? 0 : p.r;   // the low-rank term and the bias go in once per tile
     int64_t mrow[2];
     int ncol[3];
 #pragma unroll
@@ -179,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int col = n0 + wn * 96 + j * 32 + fr;
-        bv[j] = (bias && col < N) ? bf16_to_f32(bias[col]) : 0.0f;
+        bv[j] = (bias && col < N && split <= 0) ? bf16_to_f32(bias[col]) : 0.0f;
     }
 
     // Buffer (third) t holds groups 2t and 2t + 1, 52 chunks: chunk c is chunk c % 26 of
@@ -395,6 +415,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
                 acc[i][j][e] = v;
             }
 
+    if constexpr (!kBf16 && !kGelu) {
+        if (split >= 0) {   // a K split: add into the zeroed fp32 tile
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int col = n0 + wn * 96 + j * 32 + fr;
+                if (col >= N) continue;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+                        if (row < M) unsafeAtomicAdd((float*)p.out + row * N + col, acc[i][j][e]);
+                    }
+            }
+            return;
+        }
+    }
     constexpr int kEsz = kBf16 ? 2 : 4;
     if (p.vec_store) {
         // rows of 16-byte segments through LDS; N * kEsz is a multiple of 16 here
@@ -530,6 +567,30 @@ bool set_lds_attr() {
                                hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes) == hipSuccess;
 }
 
+// Zero fp32 output tiles t >= nfull (those summed over K splits), one workgroup per tile.
+__global__ __launch_bounds__(256) void zero_tiles_kernel(float* __restrict__ out, int64_t M, int N,
+                                                         int nfull) {
+    const int num_m = (int)((M + kBM - 1) / kBM), num_n = (N + kBN - 1) / kBN;
+    int pid_m, pid_n;
+    tile_of(nfull + blockIdx.x, pid_m, pid_n, num_m, num_n);
+    for (int idx = threadIdx.x; idx < kBM * kBN; idx += 256) {
+        const int64_t row = (int64_t)pid_m * kBM + idx / kBN;
+        const int col = pid_n * kBN + idx % kBN;
+        if (row < M && col < N) out[row * N + col] = 0.0f;
+    }
+}
+
+int cu_count() {
+    static int n[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (n[dev] == 0) {
+        int c = 0;
+        n[dev] = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0 ? c : 256;
+    }
+    return n[dev];
+}
+
 bool gemm_w4a4_fp6_init() {
     static int ok = -1;
     if (ok < 0)
@@ -540,10 +601,26 @@ bool gemm_w4a4_fp6_init() {
 
 void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st) {
     const int num_m = (int)((a.M + kBM - 1) / kBM), num_n = (a.N + kBN - 1) / kBN;
-    const dim3 grid(num_m * num_n), block(kThreads);
+    const int nt = num_m * num_n, G = a.K >> 6;
     PackedGemmArgs b = a;
     const int esz = a.out_bf16 ? 2 : 4;
     b.vec_store = ((int64_t)a.N * esz) % 16 == 0 && (reinterpret_cast<uintptr_t>(a.out) % 16) == 0;
+    // One tile per CU and round: when the last round would be at most a quarter full, its
+    // tiles are split over K so that it fills the GPU (fp32 output without GELU only: the
+    // splits add into a zeroed tile; the sum order of the splits is not fixed).
+    b.nfull = nt;
+    b.nsplit = 1;
+    b.gsplit = G;
+    const int ncu = cu_count();
+    const int last = nt % ncu;
+    if (!a.out_bf16 && a.act_fn == 0 && nt > ncu && last > 0 && 4 * last <= ncu && G >= 16) {
+        const int want = min(8, ncu / last);
+        b.gsplit = (G + want - 1) / want;
+        b.nsplit = (G + b.gsplit - 1) / b.gsplit;
+        b.nfull = nt - last;
+        hipLaunchKernelGGL(zero_tiles_kernel, dim3(last), dim3(256), 0, st, (float*)a.out, a.M, a.N, b.nfull);
+    }
+    const dim3 grid(b.nfull + (nt - b.nfull) * b.nsplit), block(kThreads);
     if (a.out_bf16) {
         if (a.act_fn == 1) hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, true>), grid, block, kSmemBytes, st, b);
         else hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, false>), grid, block, kSmemBytes, st, b);

@@ -61,6 +61,7 @@ struct PackedGemmArgs {
     int out_bf16;
     void* out;
     int vec_store;     // set by the launcher
+    int nfull, nsplit, gsplit;   // K split of the last round's tiles (set by the launcher)
 };
 
 void launch_quantize_act(const QuantArgs& a, hipStream_t st);

@@ -178,7 +178,12 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
  *   [N, K/64] fp32 -> prepacked, once per layer.
  * svdq_gemm_w4a4_packed: as svdq_gemm_w4a4 (INT4) on packed operands.  The result equals
  *   svdq_gemm_w4a4's up to fp32 rounding order and the three-term split of each scale
- *   product (relative error of one group's scale product a few fp32 ulp).
+ *   product (relative error of one group's scale product a few fp32 ulp).  The output is
+ *   computed in 256x192 tiles, one per compute unit at a time; with fp32 output and no
+ *   activation, when the last round of tiles would fill at most a quarter of the compute
+ *   units, those tiles are split over K and their partial sums added into the (first
+ *   zeroed) output with fp32 atomics, so their values may differ in the last bits from run
+ *   to run.  Every other case is bit-reproducible.
  * All enqueue on `stream`.
  */
 svdq_status svdq_act_packed_bytes(const svdq_layer_cfg* cfg, int64_t M, int64_t* bytes);

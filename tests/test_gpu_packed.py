@@ -4,7 +4,8 @@ CPU oracle.
 * svdq_gemm_w4a4_packed, fed the oracle-format operands through svdq_pack_act and
   svdq_prepack_weight, on shapes spanning several 256x192 tiles, ragged M and N, K from one
   group to 16, fewer groups than pipeline stages, ranks 0..128, bias, GELU and both output
-  types.  Bar: relative Frobenius error <= 1e-3 of the oracle's fp64 result (fp32 output);
+  types, and the K split of a nearly empty last round of tiles (fp32 output).  Bar: relative
+  Frobenius error <= 1e-3 of the oracle's fp64 result (fp32 output);
   bf16 output within one bf16 ulp (plus 2^-16 of the largest magnitude), >= 99% equal to
   the oracle rounded to bf16.
 * svdq_prepack_l1: the reordered low-rank factor against the layout written out on the host.
@@ -89,6 +90,28 @@ def test_packed_matches_reference_kernel_and_is_deterministic():
     assert np.array_equal(y1, y2)
     y0 = gu.host(gu.gemm(ca, sa, cw, sw, lora, l2, b))
     assert gu.rel_fro(y1, y0) <= 1e-4
+
+
+@pytest.mark.parametrize("M,N", [(4352, 3072), (4300, 3000)])
+def test_packed_gemm_k_split_last_round(M, N):
+    """17 x 16 output tiles on a 256-CU GPU: the last round's 16 tiles run as 8 K splits each,
+    added into the zeroed fp32 output.  The whole output against the nibble-operand kernel
+    (a different code path, itself checked against the oracle), samples against the oracle
+    (rows of the split tiles and of whole tiles); bf16 output (no split) at the samples."""
+    K, r = 1024, 32
+    rng = np.random.default_rng(710 + M + N)
+    ca, sa, cw, sw, lora, l2, b = _inputs(rng, M, N, K, r)
+    print(f"packed gemm K split M={M} N={N} K={K} r={r}", flush=True)
+    packed = gu.prepack(cw, sw, K, N)
+    y = gu.host(gu.gemm_prepacked(ca, sa, packed, N, lora, l2, b))
+    y0 = gu.host(gu.gemm(ca, sa, cw, sw, lora, l2, b))
+    assert gu.rel_fro(y, y0) <= 1e-5
+    mi = np.concatenate([rng.integers(4096, M, 600), rng.integers(0, 4096, 200)])
+    ni = rng.integers(0, N, mi.shape[0])
+    ref = oracle.gemm_w4a4_int4_at(mi, ni, ca, sa, cw, sw, lora, l2, b)
+    assert gu.rel_fro(y[mi, ni], ref) <= 1e-5
+    yb = gu.host(gu.gemm_prepacked(ca, sa, packed, N, lora, l2, b, out_bf16=True))
+    gu.assert_bf16_close(yb[mi, ni], ref)
 
 
 @pytest.mark.parametrize("M,K,r", [(1, 64, 0), (100, 192, 16), (256, 512, 32), (300, 1024, 32),
