@@ -567,16 +567,30 @@ bool set_lds_attr() {
                                hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes) == hipSuccess;
 }
 
-// Zero fp32 output tiles t >= nfull (those summed over K splits), one workgroup per tile.
+// Zero fp32 output tiles t >= nfull (those summed over K splits): workgroup b clears rows
+// 16 (b % 16) .. + 15 of tile nfull + b / 16, with 16-byte stores when rows allow them.
 __global__ __launch_bounds__(256) void zero_tiles_kernel(float* __restrict__ out, int64_t M, int N,
-                                                         int nfull) {
+                                                         int nfull, int vec) {
     const int num_m = (int)((M + kBM - 1) / kBM), num_n = (N + kBN - 1) / kBN;
     int pid_m, pid_n;
-    tile_of(nfull + blockIdx.x, pid_m, pid_n, num_m, num_n);
-    for (int idx = threadIdx.x; idx < kBM * kBN; idx += 256) {
-        const int64_t row = (int64_t)pid_m * kBM + idx / kBN;
-        const int col = pid_n * kBN + idx % kBN;
-        if (row < M && col < N) out[row * N + col] = 0.0f;
+    tile_of(nfull + (int)(blockIdx.x >> 4), pid_m, pid_n, num_m, num_n);
+    const int64_t r0 = (int64_t)pid_m * kBM + 16 * (blockIdx.x & 15);
+    const int c0 = pid_n * kBN;
+    if (vec) {   // N % 4 == 0 and a 16-byte aligned output
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int idx = threadIdx.x + 256 * k;   // 16 rows x 48 float4
+            const int64_t row = r0 + idx / 48;
+            const int col = c0 + 4 * (idx % 48);
+            if (row < M && col < N)
+                *reinterpret_cast<float4*>(out + row * N + col) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+        for (int idx = threadIdx.x; idx < 16 * kBN; idx += 256) {
+            const int64_t row = r0 + idx / kBN;
+            const int col = c0 + idx % kBN;
+            if (row < M && col < N) out[row * N + col] = 0.0f;
+        }
     }
 }
 
@@ -618,7 +632,8 @@ void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st) {
         b.gsplit = (G + want - 1) / want;
         b.nsplit = (G + b.gsplit - 1) / b.gsplit;
         b.nfull = nt - last;
-        hipLaunchKernelGGL(zero_tiles_kernel, dim3(last), dim3(256), 0, st, (float*)a.out, a.M, a.N, b.nfull);
+        hipLaunchKernelGGL(zero_tiles_kernel, dim3(16 * last), dim3(256), 0, st, (float*)a.out, a.M, a.N,
+                           b.nfull, b.vec_store);
     }
     const dim3 grid(b.nfull + (nt - b.nfull) * b.nsplit), block(kThreads);
     if (a.out_bf16) {

@@ -92,7 +92,7 @@ def test_packed_matches_reference_kernel_and_is_deterministic():
     assert gu.rel_fro(y1, y0) <= 1e-4
 
 
-@pytest.mark.parametrize("M,N", [(4352, 3072), (4300, 3000)])
+@pytest.mark.parametrize("M,N", [(4352, 3072), (4300, 2998)])
 def test_packed_gemm_k_split_last_round(M, N):
     """17 x 16 output tiles on a 256-CU GPU: the last round's 16 tiles run as 8 K splits each,
     added into the zeroed fp32 output.  The whole output against the nibble-operand kernel
