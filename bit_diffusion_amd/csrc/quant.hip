@@ -202,37 +202,27 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v) {
     return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
-// Sum the waves' partial low-rank products in a fixed tree order and store bf16 lora_act.
-// red holds kQWaves / 2 x RB x 256 floats.
+// Sum the waves' partial low-rank products in a fixed order (wave 0 first) and store bf16
+// lora_act: every wave writes its partials, one barrier, then wave w sums its eighth of the
+// outputs over the 8 partials.  red holds kQWaves x RB x 256 floats.
 template <int RB>
 __device__ __forceinline__ void lowrank_finish(f32x4 (&acc)[RB > 0 ? RB : 1], float* red,
                                                int64_t m0, int64_t M, uint16_t* lora) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if constexpr (RB > 0) {
 #pragma unroll
-        for (int half = kQWaves / 2; half >= 1; half >>= 1) {
-            if (wave >= half && wave < 2 * half) {
+        for (int b = 0; b < RB; ++b)
+            *reinterpret_cast<f32x4*>(&red[((wave * RB + b) * 64 + lane) * 4]) = acc[b];
+        __syncthreads();
+        // outputs: RB x 64 lanes x 4 values; this wave takes values e = wave (mod 8)
+        constexpr int kOut = RB * 256;
+        for (int o = wave * 64 + lane; o < kOut; o += kQWaves * 64) {
+            float sum = red[o];
 #pragma unroll
-                for (int b = 0; b < RB; ++b)
-                    *reinterpret_cast<f32x4*>(&red[(((wave - half) * RB + b) * 64 + lane) * 4]) = acc[b];
-            }
-            __syncthreads();
-            if (wave < half) {
-#pragma unroll
-                for (int b = 0; b < RB; ++b)
-                    acc[b] += *reinterpret_cast<const f32x4*>(&red[((wave * RB + b) * 64 + lane) * 4]);
-            }
-            __syncthreads();
-        }
-        if (wave == 0) {
-            // 16x16 output layout: lane holds rows 4 * (lane / 16) + i, column lane % 16
-#pragma unroll
-            for (int b = 0; b < RB; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t m = m0 + 4 * (lane >> 4) + i;
-                    if (m < M) lora[m * (RB * 16) + b * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(acc[b][i]);
-                }
+            for (int w = 1; w < kQWaves; ++w) sum += red[w * kOut + o];
+            const int b = o / 256, l = (o / 4) % 64, i = o % 4;
+            const int64_t m = m0 + 4 * (l >> 4) + i;
+            if (m < M) lora[m * (RB * 16) + b * 16 + (l & 15)] = (uint16_t)f32_to_bf16(sum);
         }
     }
 }
@@ -308,7 +298,7 @@ __device__ __forceinline__ void quantize_half(const Stage<RB>& st, const float* 
 template <int RB, int MODE>
 __global__ __launch_bounds__(kQThreads) void quant_act_kernel(QuantArgs p) {
     constexpr int NA = kAhead<RB>;
-    __shared__ __align__(16) float red[(kQWaves / 2) * (RB > 0 ? RB : 1) * 256];
+    __shared__ __align__(16) float red[kQWaves * (RB > 0 ? RB : 1) * 256];
     __shared__ __align__(16) float si_lds[kQWaves][NA][kStep];
     const int K = p.K, G = K >> 6;
     const int64_t M = p.M;
