@@ -19,12 +19,16 @@
 // groups; while one buffer computes, the next one's copies land and the copies of the one
 // after are issued, spread over the computation.
 //
-// Per group and 32x32 tile the two MFMAs of the next tile are issued around the fmas of
-// the current one, so a wave keeps its MFMA pipe and its VALU busy at the same time.
+// The two groups of a buffer run as one software pipeline of twelve 32x32 sub-tiles: the
+// two MFMAs of sub-tile q+1 are issued around the fmas of sub-tile q, across the group
+// boundary too, and the second group's operands are read from LDS while the first group's
+// last column computes.  Copy source addresses are kept in SGPRs.
 //
 // Tiling: 256x192 output tile per 512-thread workgroup, 8 waves as 4 x 2, each 64x96 =
-// 2 x 3 tiles of 32x32.  Workgroup ids are remapped so the workgroups an XCD runs at once
-// cover a compact block of tiles and share its L2.
+// 2 x 3 tiles of 32x32 (two waves per SIMD, whose MFMA and VALU work overlap).  Workgroup
+// ids are remapped so the workgroups an XCD runs at once cover a compact block of tiles and
+// share its L2.  With fp32 output and no activation, a last round of tiles that would fill
+// at most a quarter of the GPU is split over K, the splits adding into a zeroed tile.
 #include "common.hpp"
 #include "launch.hpp"
 #include "packed_layout.hpp"
