@@ -6,7 +6,7 @@ GEMM (per-group dequantization, low-rank up-projection, bias), for the DiT atten
 projection at 1024x1024 image scale: M = 4096 tokens, K = N = 3072, rank 32, INT4 groups
 of 64, bf16 bias, bf16 output.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline] [--only-main]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 40] [--no-cpu-baseline] [--only-main]
     python bench.py --copy-calibration      # plain 256 MiB device copies (counter calibration)
 
 The timed region is one replay of a HIP graph that holds exactly `--steps` steps (captured
@@ -51,7 +51,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps first (the clocks settle over the first few ms of load)")
     ap.add_argument("--copies", type=int, default=10,
                     help="rotating input sets (each ~30 MB) to defeat the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
