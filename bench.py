@@ -21,7 +21,8 @@ avoids not counted), with every input already in HBM.  Inputs rotate through eno
 the AWQ W4A16 GEMV of the adaLN modulation (M=2, K=3072, N=18432; GB/s against HBM) and the
 NVFP4 fused-QKV linear (M=4096, K=3072, N=9216, rank 32; TOPS against the bf16 and FP4
 peaks), and the MLP block (M=4608, 3072 -> 12288 -> 3072, fc1 with GELU and bf16 output
-feeding fc2's activation kernel; TOPS).  `roofline.traffic` comes from the HBM byte counters recorded for the GEMM kernel
+feeding fc2's activation kernel; TOPS), and the attention projection with a rank-16 LoRA
+adapter merged into its low-rank branch (eager step time next to ms_per_step_eager).  `roofline.traffic` comes from the HBM byte counters recorded for the GEMM kernel
 (profiles/), and is null when the kernel's sources changed since they were taken.
 """
 import argparse
@@ -266,6 +267,45 @@ def mlp_leg(steps, sp, stream):
             "fc2_quantize_GBs": round(q2_bytes / (ms_q2 * 1e-3) / 1e9, 1)}
 
 
+def lora_leg(steps, sp, stream, si, sets):
+    """The attention projection with a rank-16 LoRA adapter merged into its low-rank branch
+    (svdq_merge_lora: rank 32 + 16 = 48), eager launches over the same rotating inputs."""
+    import torch
+    import bit_diffusion_amd as bd
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(41)
+    rl = 16
+    ro = bd.svdq_merged_rank(R, rl)
+    cfg = bd.LayerCfg.make(K, N, R)
+    cfgm = bd.LayerCfg.make(K, N, ro)
+    down = (torch.randn((rl, K), device=dev, generator=g) * 0.02).to(torch.bfloat16).view(torch.int16)
+    up = (torch.randn((N, rl), device=dev, generator=g) * 0.02).to(torch.bfloat16).view(torch.int16)
+    merged = []
+    for s in sets:
+        l1m = torch.empty((ro, K), dtype=torch.int16, device=dev)
+        l2m = torch.empty((N, ro), dtype=torch.int16, device=dev)
+        bd.svdq_merge_lora(cfg, rl, s["l1"], s["l2"], down, up, 0.5, l1m, l2m)
+        l1p = torch.empty(bd.svdq_prepacked_l1_bytes(cfgm), dtype=torch.uint8, device=dev)
+        bd.svdq_prepack_l1(cfgm, l1m, l1p)
+        merged.append(dict(l1p=l1p, l2=l2m, lora=torch.empty((M, ro), dtype=torch.int16, device=dev)))
+
+    def go(i):
+        s, m = sets[i % len(sets)], merged[i % len(sets)]
+        bd.svdq_quantize_act_packed(cfgm, M, s["x"], si, m["l1p"], s["apacked"], s["scales"],
+                                    m["lora"], sp)
+        bd.svdq_gemm_w4a4_packed(cfgm, M, s["apacked"], s["packed"], m["lora"], m["l2"],
+                                 s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16, s["out"], sp)
+
+    for i in range(len(sets)):
+        go(i)
+    torch.cuda.synchronize()
+    ms = time_launches(go, steps, stream)
+    ops = 2.0 * M * N * K + 2.0 * M * N * ro + 2.0 * M * K * ro
+    return {"workload": f"attn_4096x3072x3072_r{R}+lora{rl}", "merged_rank": ro,
+            "ms_per_step_eager": round(ms, 5), "TOPS": round(ops / (ms * 1e-3) / 1e12, 2)}
+
+
 def make_inputs(copies):
     """Synthetic inputs of the attention-projection workload, on the GPU.
 
@@ -468,6 +508,7 @@ def main():
         out["awq"] = awq_leg(args.steps, sp, stream)
         out["nvfp4"] = nvfp4_leg(args.steps, sp, stream)
         out["mlp"] = mlp_leg(args.steps, sp, stream)
+        out["lora"] = lora_leg(args.steps, sp, stream, si, sets)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     print(json.dumps(out), flush=True)

@@ -19,7 +19,7 @@ __all__ = [
     "svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_device",
     "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
     "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
-    "svdq_prepacked_l1_bytes", "svdq_prepack_l1",
+    "svdq_prepacked_l1_bytes", "svdq_prepack_l1", "svdq_merged_rank", "svdq_merge_lora",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -84,6 +84,16 @@ def svdq_prepacked_weight_bytes(cfg):
     n = ctypes.c_int64(0)
     _check(lib().svdq_prepacked_weight_bytes(ctypes.byref(cfg), ctypes.byref(n)))
     return n.value
+
+
+def svdq_merged_rank(rank, r_lora):
+    return int(lib().svdq_merged_rank(int(rank), int(r_lora)))
+
+
+def svdq_merge_lora(cfg, r_lora, l1, l2, lora_down, lora_up, alpha, l1_out, l2_out, stream=None):
+    return _check(lib().svdq_merge_lora(ctypes.byref(cfg), int(r_lora), _ptr(l1), _ptr(l2),
+                                        _ptr(lora_down), _ptr(lora_up), float(alpha),
+                                        _ptr(l1_out), _ptr(l2_out), _stream(stream)))
 
 
 def svdq_prepacked_l1_bytes(cfg):

@@ -228,6 +228,35 @@ svdq_status svdq_prepacked_weight_bytes(const svdq_layer_cfg* cfg, int64_t* byte
     return SVDQ_OK;
 }
 
+svdq_status svdq_merge_lora(const svdq_layer_cfg* cfg, int32_t r_lora, const void* l1,
+                            const void* l2, const void* lora_down, const void* lora_up,
+                            float alpha, void* l1_out, void* l2_out, svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    if (r_lora <= 0) return fail(SVDQ_ERR_INVALID_ARG, "r_lora = %d must be positive", r_lora);
+    const int ro = svdq_merged_rank(cfg->rank, r_lora);
+    if (ro > 128)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "merged rank %d exceeds the supported maximum 128", ro);
+    if (!std::isfinite(alpha)) return fail(SVDQ_ERR_INVALID_ARG, "alpha is not finite");
+    if (cfg->rank > 0) {
+        SVDQ_TRY(check_ptr(l1, "l1", 2));
+        SVDQ_TRY(check_ptr(l2, "l2", 2));
+    }
+    SVDQ_TRY(check_ptr(lora_down, "lora_down", 2));
+    SVDQ_TRY(check_ptr(lora_up, "lora_up", 2));
+    SVDQ_TRY(check_ptr(l1_out, "l1_out", 2));
+    SVDQ_TRY(check_ptr(l2_out, "l2_out", 2));
+    SVDQ_TRY(check_current_device());
+    svdq::launch_merge_lora(cfg->in_features, cfg->out_features, cfg->rank, r_lora, ro, l1, l2,
+                            lora_down, lora_up, alpha, l1_out, l2_out,
+                            reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_merge_lora");
+}
+
+int32_t svdq_merged_rank(int32_t rank, int32_t r_lora) {
+    if (rank < 0 || r_lora < 0) return -1;
+    return (rank + r_lora + 15) / 16 * 16;
+}
+
 svdq_status svdq_prepacked_l1_bytes(const svdq_layer_cfg* cfg, int64_t* bytes) {
     SVDQ_TRY(check_cfg(cfg));
     SVDQ_TRY(check_int4(cfg));

@@ -71,6 +71,9 @@ void launch_awq_gemv(const AwqArgs& a, hipStream_t st);
 
 void launch_prepack_wgt(int N, int K, const void* wcodes, const void* wscales, void* out,
                         hipStream_t st);
+void launch_merge_lora(int K, int N, int r, int rl, int ro, const void* l1, const void* l2,
+                       const void* down, const void* up, float alpha, void* l1o, void* l2o,
+                       hipStream_t st);
 int64_t prepacked_l1_bytes(int r, int K);
 void launch_prepack_l1(int r, int K, const void* l1, void* out, hipStream_t st);
 void launch_pack_act(int64_t M, int K, const void* acodes, const void* ascales, void* out,

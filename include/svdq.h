@@ -204,6 +204,28 @@ svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const vo
                                   const void* bias, int32_t act, int32_t out_dtype, void* out,
                                   svdq_stream_t stream);
 
+/* LoRA adapters through the low-rank branch (page "Diffusers integra Nunchaku ...",
+ * "Nunchaku Lite: integración y modelo de ejecución": LoRA keeps working because the module
+ * structure is kept; page "Diffusers Natively Integrates Nunchaku Lite ...", the paragraph
+ * on loading through from_pretrained()).  An adapter y += alpha (x A^T) B^T is a term of the
+ * branch's own form, so it is merged into the branch's factors once, after which
+ * svdq_quantize_act / svdq_prepack_l1 and the GEMMs run unchanged at the merged rank:
+ *
+ *   l1_out [r', K] = [l1; lora_down; 0]          (bf16, row-major)
+ *   l2_out [N, r'] = [l2 | bf16(alpha lora_up) | 0]
+ *
+ * with r = cfg->rank, lora_down = A bf16 [r_lora, K], lora_up = B bf16 [N, r_lora], and
+ * r' = svdq_merged_rank(r, r_lora) = r + r_lora rounded up to a multiple of 16 (the padding
+ * rows and columns are zero and add exact zeros).  alpha lora_up is one fp32 product per
+ * element rounded to nearest-even bf16.  r' must not exceed 128 (else
+ * SVDQ_ERR_UNSUPPORTED_CONFIG); r_lora >= 1 and alpha finite (else SVDQ_ERR_INVALID_ARG).
+ * l1 and l2 may be NULL when r = 0.  Device buffers, caller-owned, 2-byte aligned;
+ * enqueued on `stream`.  svdq_merged_rank returns -1 for a negative argument. */
+int32_t svdq_merged_rank(int32_t rank, int32_t r_lora);
+svdq_status svdq_merge_lora(const svdq_layer_cfg* cfg, int32_t r_lora, const void* l1,
+                            const void* l2, const void* lora_down, const void* lora_up,
+                            float alpha, void* l1_out, void* l2_out, svdq_stream_t stream);
+
 /* SVDQ_OK when HIP device `device` is a gfx950 GPU, else SVDQ_ERR_UNSUPPORTED_DEVICE
  * (or SVDQ_ERR_INVALID_ARG for a bad ordinal).  Results are cached per device. */
 svdq_status svdq_check_device(int device);

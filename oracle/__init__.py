@@ -175,6 +175,31 @@ def gemm_w4a4_int4_at(mi, ni, ca, sa, cw, sw, lora=None, l2=None, bias=None, act
     return out
 
 
+def merge_lora(l1, l2, lora_down, lora_up, alpha):
+    """A LoRA adapter y += alpha (x A^T) B^T merged into the low-rank branch (page "Diffusers
+    integra Nunchaku ...", "Nunchaku Lite: integración y modelo de ejecución": LoRA keeps
+    working with the SVDQ modules).  The branch computes lora_act = x l1^T and adds
+    lora_act l2^T, so the adapter is appended to its factors: l1' = [l1; A; 0],
+    l2' = [l2 | bf16(alpha B) | 0], the rank padded with zeros to a multiple of 16.  alpha B
+    is one fp32 product per element, rounded to nearest-even bf16.  l1 [r, K], l2 [N, r] (or
+    None for r = 0), A [rl, K], B [N, rl]: bf16 bit patterns."""
+    down = _c(lora_down, np.uint16)
+    up = _c(lora_up, np.uint16)
+    rl, K = down.shape
+    N = up.shape[0]
+    r = 0 if l1 is None else l1.shape[0]
+    ro = (r + rl + 15) // 16 * 16
+    l1o = np.zeros((ro, K), np.uint16)
+    l2o = np.zeros((N, ro), np.uint16)
+    if r:
+        l1o[:r] = l1
+        l2o[:, :r] = l2
+    l1o[r:r + rl] = down
+    prod = np.float32(alpha) * bf16_to_f64(up).astype(np.float32)   # fp32 product
+    l2o[:, r:r + rl] = bf16_from_f64(prod.astype(np.float64))
+    return l1o, l2o
+
+
 # ------------------------------------------------------------------ NVFP4
 
 def quant_act_nvfp4(x_bf16, smooth_inv, S, l1_bf16=None):

@@ -133,6 +133,23 @@ def test_prepacked_l1_size_and_bad_args():
     assert "l1_packed" in bd.svdq_last_error()
 
 
+def test_merge_lora_rank_rules():
+    assert bd.svdq_merged_rank(32, 16) == 48 and bd.svdq_merged_rank(16, 5) == 32
+    assert bd.svdq_merged_rank(0, 1) == 16 and bd.svdq_merged_rank(-1, 4) == -1
+    L = bd.lib()
+    cfg = bd.LayerCfg.make(512, 512, 112)
+    # 112 + 32 -> 144 > 128
+    assert L.svdq_merge_lora(ctypes.byref(cfg), 32, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE,
+                             None) == bd.SVDQ_ERR_UNSUPPORTED_CONFIG
+    assert L.svdq_merge_lora(ctypes.byref(cfg), 0, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE,
+                             None) == bd.SVDQ_ERR_INVALID_ARG
+    cfg16 = bd.LayerCfg.make(512, 512, 16)
+    assert L.svdq_merge_lora(ctypes.byref(cfg16), 8, FAKE, FAKE, None, FAKE, 1.0, FAKE, FAKE,
+                             None) == bd.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_merge_lora(ctypes.byref(cfg16), 8, FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE,
+                             FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
+
+
 def test_python_binding_raises_with_message():
     cfg = bd.LayerCfg.make(100, 512, 16)
     with pytest.raises(bd.SvdqError) as e:
