@@ -199,7 +199,8 @@ def nvfp4_leg(steps, sp, stream):
 def mlp_leg(steps, sp, stream):
     """DiT MLP block on the packed path (M=4608 tokens, 3072 -> 12288 -> 3072, rank 32):
     fc1 with GELU(tanh) in its epilogue writing bf16, then fc2's activation kernel reads that
-    output and fc2 writes fp32.  Weights are this library's own quantization of bf16
+    output and fc2 writes fp32; and the same block with fc2's activation kernel fused into
+    fc1's epilogue (the bf16 intermediate never stored).  Weights are this library's own quantization of bf16
     N(0, 0.02) draws; activations bf16 N(0, 1) with 31 outlier channels x50."""
     import torch
     import bit_diffusion_amd as bd
@@ -222,9 +223,10 @@ def mlp_leg(steps, sp, stream):
         bd.svdq_quantize_act(cw, N, w, ones, None, 1.0, wc, ws, None)
         packed = torch.empty(bd.svdq_prepacked_weight_bytes(cw), dtype=torch.uint8, device=dev)
         bd.svdq_prepack_weight(cw, wc, ws, packed)
+        l1 = bf16((Rm, K), 0.02)
         l1p = torch.empty(bd.svdq_prepacked_l1_bytes(cfg), dtype=torch.uint8, device=dev)
-        bd.svdq_prepack_l1(cfg, bf16((Rm, K), 0.02), l1p)
-        return dict(cfg=cfg, packed=packed, l1p=l1p, l2=bf16((N, Rm), 0.02), bias=bf16((N,), 0.02),
+        bd.svdq_prepack_l1(cfg, l1, l1p)
+        return dict(cfg=cfg, packed=packed, l1=l1, l1p=l1p, l2=bf16((N, Rm), 0.02), bias=bf16((N,), 0.02),
                     si=torch.rand(K, device=dev, generator=g) + 0.5,
                     apk=torch.empty(bd.svdq_act_packed_bytes(cfg, Mm), dtype=torch.uint8, device=dev),
                     lora=torch.empty((Mm, Rm), dtype=torch.int16, device=dev))
@@ -248,11 +250,32 @@ def mlp_leg(steps, sp, stream):
         quant(fc2, h)
         gemm(fc2, bd.SVDQ_ACT_NONE, bd.SVDQ_DT_F32, y)
 
+    work = torch.empty((Mm, Rm), dtype=torch.float32, device=dev)
+    yf = torch.empty_like(y)
+
+    def fc1_fused():
+        bd.svdq_gemm_w4a4_packed_quantize_next(
+            fc1["cfg"], Mm, fc1["apk"], fc1["packed"], fc1["lora"], fc1["l2"], fc1["bias"],
+            bd.SVDQ_ACT_GELU_TANH, fc2["cfg"], fc2["si"], fc2["l1"], fc2["apk"], None, fc2["lora"],
+            work, sp)
+
+    def go_fused(i):   # fc2's activation kernel runs inside fc1's GEMM epilogue
+        quant(fc1, x)
+        fc1_fused()
+        gemm(fc2, bd.SVDQ_ACT_NONE, bd.SVDQ_DT_F32, yf)
+
     go(0)
+    go_fused(0)
     torch.cuda.synchronize()
+    # the two orders of the same block agree up to the fp32 order of fc2's down-projection
+    fused_rel = float((yf - y).double().norm() / y.double().norm())
+    if not fused_rel <= 1e-3:
+        raise RuntimeError(f"fused MLP differs from the unfused block: rel {fused_rel:.3e}")
     n = max(3, steps // 5)
     ms = time_launches(go, n, stream)
+    ms_fused = time_launches(go_fused, n, stream)
     ms_fc1 = time_launches(lambda i: gemm(fc1, bd.SVDQ_ACT_GELU_TANH, bd.SVDQ_DT_BF16, h), n, stream)
+    ms_fc1f = time_launches(lambda i: fc1_fused(), n, stream)
     ms_q2 = time_launches(lambda i: quant(fc2, h), n, stream)
     ops1 = 2.0 * Mm * N1 * K1 + 2.0 * Mm * N1 * Rm
     ops2 = 2.0 * Mm * N2 * K2 + 2.0 * Mm * N2 * Rm
@@ -264,7 +287,11 @@ def mlp_leg(steps, sp, stream):
             "fc1_gelu_bf16_gemm_ms": round(ms_fc1, 4),
             "fc1_gelu_bf16_gemm_TOPS": round(ops1 / (ms_fc1 * 1e-3) / 1e12, 2),
             "fc2_quantize_ms": round(ms_q2, 4),
-            "fc2_quantize_GBs": round(q2_bytes / (ms_q2 * 1e-3) / 1e9, 1)}
+            "fc2_quantize_GBs": round(q2_bytes / (ms_q2 * 1e-3) / 1e9, 1),
+            "ms_per_mlp_fused": round(ms_fused, 4),
+            "fused_TOPS": round(ops / (ms_fused * 1e-3) / 1e12, 2),
+            "fc1_gemm_quantize_next_ms": round(ms_fc1f, 4),
+            "fused_vs_unfused_rel": float(f"{fused_rel:.3e}")}
 
 
 def lora_leg(steps, sp, stream, si, sets):

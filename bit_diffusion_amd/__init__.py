@@ -20,6 +20,7 @@ __all__ = [
     "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
     "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
     "svdq_prepacked_l1_bytes", "svdq_prepack_l1", "svdq_merged_rank", "svdq_merge_lora",
+    "svdq_gemm_w4a4_packed_quantize_next",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -129,6 +130,17 @@ def svdq_gemm_w4a4_packed(cfg, M, act_packed, prepacked, lora_act, l2, bias, act
     return _check(lib().svdq_gemm_w4a4_packed(
         ctypes.byref(cfg), int(M), _ptr(act_packed), _ptr(prepacked), _ptr(lora_act), _ptr(l2),
         _ptr(bias), int(act), int(out_dtype), _ptr(out), _stream(stream)))
+
+
+def svdq_gemm_w4a4_packed_quantize_next(cfg, M, act_packed, prepacked, lora_act, l2, bias, act,
+                                        next_cfg, next_smooth_inv, next_l1, next_act_packed,
+                                        next_act_scales, next_lora_act, lora_workspace,
+                                        stream=None):
+    return _check(lib().svdq_gemm_w4a4_packed_quantize_next(
+        ctypes.byref(cfg), int(M), _ptr(act_packed), _ptr(prepacked), _ptr(lora_act), _ptr(l2),
+        _ptr(bias), int(act), ctypes.byref(next_cfg), _ptr(next_smooth_inv), _ptr(next_l1),
+        _ptr(next_act_packed), _ptr(next_act_scales), _ptr(next_lora_act), _ptr(lora_workspace),
+        _stream(stream)))
 
 
 def svdq_check_device(device=0):

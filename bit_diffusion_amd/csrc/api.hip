@@ -370,6 +370,58 @@ svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const vo
     return after_launch("svdq_gemm_w4a4_packed");
 }
 
+svdq_status svdq_gemm_w4a4_packed_quantize_next(
+    const svdq_layer_cfg* cfg, int64_t M, const void* act_packed, const void* prepacked,
+    const void* lora_act, const void* l2, const void* bias, int32_t act,
+    const svdq_layer_cfg* next_cfg, const float* next_smooth_inv, const void* next_l1,
+    void* next_act_packed, float* next_act_scales, void* next_lora_act, float* lora_workspace,
+    svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    SVDQ_TRY(check_cfg(next_cfg));
+    SVDQ_TRY(check_int4(next_cfg));
+    if (next_cfg->in_features != cfg->out_features)
+        return fail(SVDQ_ERR_INVALID_ARG, "next layer in_features %d != this layer's out_features %d",
+                    next_cfg->in_features, cfg->out_features);
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
+        return fail(SVDQ_ERR_INVALID_ARG, "act %d is not a svdq_act value", act);
+    SVDQ_TRY(check_ptr(act_packed, "act_packed", 16));
+    SVDQ_TRY(check_ptr(prepacked, "prepacked", 16));
+    if (cfg->rank > 0) {
+        SVDQ_TRY(check_ptr(lora_act, "lora_act", 16));
+        SVDQ_TRY(check_ptr(l2, "l2", 16));
+    }
+    if (bias != nullptr && !aligned(bias, 2)) return fail(SVDQ_ERR_INVALID_ARG, "bias is not 2-byte aligned");
+    SVDQ_TRY(check_ptr(next_smooth_inv, "next_smooth_inv", 16));
+    SVDQ_TRY(check_ptr(next_act_packed, "next_act_packed", 16));
+    if (next_act_scales != nullptr && !aligned(next_act_scales, 4))
+        return fail(SVDQ_ERR_INVALID_ARG, "next_act_scales is not 4-byte aligned");
+    if (next_cfg->rank > 0) {
+        SVDQ_TRY(check_ptr(next_l1, "next_l1", 16));
+        SVDQ_TRY(check_ptr(next_lora_act, "next_lora_act", 2));
+        SVDQ_TRY(check_ptr(lora_workspace, "lora_workspace", 4));
+    }
+    const int64_t tiles = ((M + 255) / 256) * ((cfg->out_features + 191) / 192);
+    if (tiles >= (int64_t)1 << 31)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
+    SVDQ_TRY(check_current_device());
+    if (M == 0) return SVDQ_OK;
+    if (!svdq::gemm_w4a4_fp6_init())
+        return fail(SVDQ_ERR_LAUNCH, "could not reserve LDS for the packed GEMM");
+    svdq::PackedGemmArgs a{M, cfg->out_features, cfg->in_features, cfg->rank, act_packed,
+                           prepacked, lora_act, l2, bias, act, 1, next_lora_act, 0};
+    a.quantize_next = 1;
+    a.next_r = next_cfg->rank;
+    a.next_si = next_smooth_inv;
+    a.next_l1 = next_l1;
+    a.next_packed = next_act_packed;
+    a.next_scales = next_act_scales;
+    a.lora_work = lora_workspace;
+    svdq::launch_gemm_w4a4_fp6(a, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_gemm_w4a4_packed_quantize_next");
+}
+
 svdq_status svdq_check_device(int device) { return check_device_ordinal(device); }
 
 svdq_status svdq_check_arch(const char* arch_name) {

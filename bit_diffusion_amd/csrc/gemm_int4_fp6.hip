@@ -32,6 +32,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "packed_layout.hpp"
+#include "quant_lane.hpp"
 
 namespace svdq {
 namespace {
@@ -137,7 +138,12 @@ __device__ __forceinline__ void work_of(const PackedGemmArgs& p, int num_m, int 
 template <bool kBf16>
 constexpr int kStgStride = kBf16 ? 208 : 416;
 
-template <bool kBf16, bool kGelu>
+// The tile as bf16 in LDS for the next layer's quantization: [256 rows][192 columns], row
+// stride 400 bytes.
+constexpr int kTileStride = 2 * kBN + 16;
+static_assert(kBM * kTileStride <= kSmemBytes, "the bf16 tile fits in the pipeline buffers");
+
+template <bool kBf16, bool kGelu, bool kNext = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmArgs p) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -419,6 +425,105 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
                 acc[i][j][e] = v;
             }
 
+    if constexpr (kNext) {
+        // The next layer's activation kernel on this tile, from the bf16 values this layer
+        // would store (page "Hugging Face 把 Nunchaku 4-bit Diffusion 接到 Diffusers",
+        // 技术细节 1 steps 1, 3, 4 applied to this output): smoothing, 64-channel groups
+        // (the tile's 192 columns are three whole groups), codes and scales in the packed
+        // layout, and this tile's share of the next low-rank down-projection.
+        static_assert(kBf16, "the next layer reads bf16");
+        barrier();   // every wave is done with the pipeline buffers
+        uint8_t* tl = smem;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int rr = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+                    const int cc = wn * 96 + j * 32 + fr;
+                    *reinterpret_cast<uint16_t*>(tl + rr * kTileStride + 2 * cc) =
+                        (uint16_t)f32_to_bf16(acc[i][j][e]);
+                }
+        barrier();
+        const int G2 = N >> 6;                    // the next layer's groups
+        const int ngr = min(3, (N - n0) >> 6);    // whole groups in this tile
+        // 24 fragments (8 blocks of 32 rows x 3 groups); wave w quantizes w, w + 8, w + 16.
+        // Lane L: row L % 32 of the block, channels 32 (L / 32) .. + 31 of the group.
+        const int h = lane >> 5, r32 = lane & 31;
+#pragma unroll 1
+        for (int jb = 0; jb < 3; ++jb) {
+            const int job = wave + 8 * jb;
+            const int rb = job & 7, gi = job >> 3;
+            if (gi >= ngr) continue;
+            const int rr = rb * 32 + r32;
+            const int64_t row = m0 + rr;
+            const int c0 = gi * 64 + 32 * h;
+            uint4 xw[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                xw[t] = row < M ? *reinterpret_cast<const uint4*>(tl + rr * kTileStride + 2 * (c0 + 8 * t))
+                                : make_uint4(0u, 0u, 0u, 0u);   // padding rows quantize to zero
+            lane::Vals v;
+            const float* si = p.next_si + n0 + c0;
+            auto smooth = [&] {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float4 s0 = *reinterpret_cast<const float4*>(si + 8 * t);
+                    const float4 s1 = *reinterpret_cast<const float4*>(si + 8 * t + 4);
+                    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                    const uint32_t w[4] = {xw[t].x, xw[t].y, xw[t].z, xw[t].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v.ev[4 * t + i] = __uint_as_float(w[i] << 16) * sv[2 * i];
+                        v.od[4 * t + i] = __uint_as_float(w[i] & 0xFFFF0000u) * sv[2 * i + 1];
+                    }
+                }
+            };
+            smooth();
+            float a = lane::absmax32(v);
+            a = fmaxf(a, __shfl_xor(a, 32, 64));   // the group's other half
+            const float s = a / 7.0f;
+            lane::int4_codes32_exact(v, s, smooth);
+            const lane::u32x6 f = lane::cvt_fp6x32(v.ev, v.od, 8.0f);
+            const int g2 = (n0 >> 6) + gi;
+            uint8_t* blk = (uint8_t*)p.next_packed + act_block(row, g2, G2);
+            *reinterpret_cast<uint4*>(blk + frag_dword(lane, 0)) = make_uint4(f[0], f[1], f[2], f[3]);
+            *reinterpret_cast<uint2*>(blk + frag_dword(lane, 4)) = make_uint2(f[4], f[5]);
+            if (h == 0) {
+                *reinterpret_cast<uint2*>(blk + kFrag + 8 * r32) = act_scale_pair(s);
+                if (row < M && p.next_scales) p.next_scales[row * G2 + g2] = s;
+            }
+        }
+        // this tile's columns' share of the next layer's lora_act = x . l1^T: wave w takes
+        // rows 32 w .. + 31; the partial sums go into the zeroed fp32 workspace
+        const int R2 = p.next_r;
+        if (R2 > 0) {
+            const uint16_t* l1n = (const uint16_t*)p.next_l1;
+            const int nks = (ngr * 64) >> 5;   // 32-channel steps
+#pragma unroll 1
+            for (int rb2 = 0; rb2 < 2; ++rb2) {
+                const int ar = wave * 32 + rb2 * 16 + (lane & 15);
+#pragma unroll 1
+                for (int jb = 0; jb < R2 / 16; ++jb) {
+                    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const uint16_t* brow = l1n + (int64_t)(16 * jb + (lane & 15)) * N + n0 + 8 * (lane >> 4);
+#pragma unroll 1
+                    for (int ks = 0; ks < nks; ++ks) {
+                        const uint4 av = *reinterpret_cast<const uint4*>(tl + ar * kTileStride + 2 * (32 * ks + 8 * (lane >> 4)));
+                        const uint4 bv4 = *reinterpret_cast<const uint4*>(brow + 32 * ks);
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv4), c, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t row = m0 + wave * 32 + rb2 * 16 + 4 * (lane >> 4) + i;
+                        if (row < M) unsafeAtomicAdd(p.lora_work + row * R2 + 16 * jb + (lane & 15), c[i]);
+                    }
+                }
+            }
+        }
+        return;
+    }
     if constexpr (!kBf16 && !kGelu) {
         if (split >= 0) {   // a K split: add into the zeroed fp32 tile
 #pragma unroll
@@ -565,9 +670,9 @@ void launch_pack_act(int64_t M, int K, const void* acodes, const void* ascales, 
                        (const uint8_t*)acodes, (const float*)ascales, (uint8_t*)out);
 }
 
-template <bool kBf16, bool kGelu>
+template <bool kBf16, bool kGelu, bool kNext = false>
 bool set_lds_attr() {
-    return hipFuncSetAttribute((const void*)gemm_w4a4_fp6_kernel<kBf16, kGelu>,
+    return hipFuncSetAttribute((const void*)gemm_w4a4_fp6_kernel<kBf16, kGelu, kNext>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes) == hipSuccess;
 }
 
@@ -598,6 +703,17 @@ __global__ __launch_bounds__(256) void zero_tiles_kernel(float* __restrict__ out
     }
 }
 
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
+// fp32 low-rank sums -> bf16 lora_act (round to nearest even)
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src,
+                                                          uint16_t* __restrict__ dst, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        dst[i] = (uint16_t)f32_to_bf16(src[i]);
+}
+
 int cu_count() {
     static int n[64] = {0};
     int dev = 0;
@@ -613,7 +729,8 @@ bool gemm_w4a4_fp6_init() {
     static int ok = -1;
     if (ok < 0)
         ok = set_lds_attr<false, false>() && set_lds_attr<false, true>() &&
-             set_lds_attr<true, false>() && set_lds_attr<true, true>();
+             set_lds_attr<true, false>() && set_lds_attr<true, true>() &&
+             set_lds_attr<true, false, true>() && set_lds_attr<true, true, true>();
     return ok == 1;
 }
 
@@ -631,7 +748,8 @@ void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st) {
     b.gsplit = G;
     const int ncu = cu_count();
     const int last = nt % ncu;
-    if (!a.out_bf16 && a.act_fn == 0 && nt > ncu && last > 0 && 4 * last <= ncu && G >= 16) {
+    if (!a.quantize_next && !a.out_bf16 && a.act_fn == 0 && nt > ncu && last > 0 && 4 * last <= ncu &&
+        G >= 16) {
         const int want = min(8, ncu / last);
         b.gsplit = (G + want - 1) / want;
         b.nsplit = (G + b.gsplit - 1) / b.gsplit;
@@ -640,6 +758,17 @@ void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st) {
                            b.nfull, b.vec_store);
     }
     const dim3 grid(b.nfull + (nt - b.nfull) * b.nsplit), block(kThreads);
+    if (a.quantize_next) {   // the next layer's low-rank sums: zeroed, added per tile, rounded
+        const int64_t nl = a.next_r > 0 ? a.M * a.next_r : 0;
+        const unsigned lb = (unsigned)std::min<int64_t>((nl + 255) / 256, 2048);
+        if (nl > 0) hipLaunchKernelGGL(zero_f32_kernel, dim3(lb), dim3(256), 0, st, a.lora_work, nl);
+        if (a.act_fn == 1) hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, true, true>), grid, block, kSmemBytes, st, b);
+        else hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, false, true>), grid, block, kSmemBytes, st, b);
+        if (nl > 0)
+            hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(lb), dim3(256), 0, st, (const float*)a.lora_work,
+                               (uint16_t*)a.out, nl);
+        return;
+    }
     if (a.out_bf16) {
         if (a.act_fn == 1) hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, true>), grid, block, kSmemBytes, st, b);
         else hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, false>), grid, block, kSmemBytes, st, b);

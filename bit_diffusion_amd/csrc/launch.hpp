@@ -62,6 +62,15 @@ struct PackedGemmArgs {
     void* out;
     int vec_store;     // set by the launcher
     int nfull, nsplit, gsplit;   // K split of the last round's tiles (set by the launcher)
+    // the next layer's activation quantization in the epilogue (quantize_next); the tile's
+    // bf16 outputs are not stored
+    int quantize_next;
+    int next_r;              // next layer's rank
+    const float* next_si;    // [N] smoothing factors of the next layer
+    const void* next_l1;     // bf16 [next_r, N] row-major, or NULL
+    void* next_packed;       // the next layer's packed activation buffer (its K = N)
+    float* next_scales;      // fp32 [M, N / 64] or NULL
+    float* lora_work;        // fp32 [M, next_r], zeroed: the next layer's low-rank sums
 };
 
 void launch_quantize_act(const QuantArgs& a, hipStream_t st);

@@ -27,6 +27,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "packed_layout.hpp"
+#include "quant_lane.hpp"
 
 // The quantizer is defined as a sequence of individually rounded fp32 operations.
 #pragma clang fp contract(off)
@@ -34,8 +35,9 @@
 namespace svdq {
 namespace {
 
+using namespace lane;
+
 constexpr int kRows = 16;
-constexpr float kMinNormal = 1.17549435e-38f;
 constexpr int kQWaves = 8;
 constexpr int kQThreads = kQWaves * 64;
 constexpr int kStep = 128;   // channels per wave step
@@ -53,8 +55,6 @@ constexpr bool kPrefetchL1 = RB <= 4;
 template <int RB>
 constexpr bool kLateL1 = RB == 2;
 
-typedef float f32x16v __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 
 template <int RB>
 struct Stage {
@@ -96,12 +96,6 @@ __device__ __forceinline__ void load_stage(Stage<RB>& st, const uint16_t* xr, co
     if (with_l1) load_stage_l1<MODE, RB>(st, l1s, c, k0);
 }
 
-// The lane's 32 values in the order of the FP6 conversion: ev[i] is channel 2i (the low
-// bf16 of word i), od[i] channel 2i + 1 (the high bf16).
-struct Vals {
-    f32x16v ev, od;
-};
-
 // x_hat = fp32(x) * smooth_inv for the lane's 32 channels (smooth_inv from the wave's LDS
 // slice).
 template <int RB>
@@ -120,58 +114,10 @@ __device__ __forceinline__ void smooth32(Vals& v, const Stage<RB>& st, const flo
     }
 }
 
-// 32 floats -> 32 FP6 E2M3 fields (value / scale, field 2i from ev[i], 2i+1 from od[i]) in
-// six dwords, one v_cvt_scalef32_2xpk16_fp6_f32.  Written as asm with an early-clobber
-// result: the instruction reads its 32 source registers over several cycles, so its six
-// result registers must not overlap them (left to itself the compiler may place them there).
-__device__ __forceinline__ u32x6 cvt_fp6x32(const f32x16v& ev, const f32x16v& od, float scale) {
-    u32x6 r;
-    asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3"
-                 : "=&v"(r) : "v"(ev), "v"(od), "v"(scale));
-    return r;
-}
-
-__device__ __forceinline__ float absmax32(const Vals& v) {
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fmaxf(fabsf(v.ev[i]), fabsf(v.od[i])));
-    return a;
-}
-
-// rne(xh / s) for the lane's 32 values, in place, with the fp32 quotient correctly rounded
-// as the code's definition requires.  The quotient is estimated as xh * (1/s) (within 2^-22
-// relative of the correctly rounded one, i.e. < 2e-6 for |q| <= 8); only when an estimate
-// lies within 4e-6 of a half-integer can the correctly rounded quotient round differently,
-// and then the lane redoes all 32 with the exact division (smooth32 recomputes x_hat).
-// s = absmax / 7 bounds |xh / s| by 7 (up to rounding), so rne never leaves [-7, 7] and the
-// definition's clamp to [-8, 7] is the identity.  Codes come out as floats with +0 for 0.
-// s = 0 (an all-zero group) gives codes 0.
-__device__ __forceinline__ float rne_keep_d(f32x16v& v, int i, float rcp, float dmax) {
-    const float y = v[i] * rcp;
-    const float d = y - __builtin_rintf(y);
-    v[i] = y - d;   // = rne(y) exactly, with +0 where it is zero
-    return fmaxf(dmax, fabsf(d));
-}
-
 template <int RB>
 __device__ __forceinline__ void int4_codes32(Vals& v, float s, const Stage<RB>& st,
                                              const float* si) {
-    const bool zero = s == 0.0f;
-    const float rcp = zero ? 0.0f : 1.0f / s;
-    float dmax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        dmax = rne_keep_d(v.ev, i, rcp, dmax);
-        dmax = rne_keep_d(v.od, i, rcp, dmax);
-    }
-    if (!zero && (dmax > 0.499996f || s < kMinNormal)) {
-        smooth32<RB>(v, st, si);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            v.ev[i] = __builtin_rintf(v.ev[i] / s) + 0.0f;
-            v.od[i] = __builtin_rintf(v.od[i] / s) + 0.0f;
-        }
-    }
+    int4_codes32_exact(v, s, [&] { smooth32<RB>(v, st, si); });
 }
 
 // Nearest E4M3 ("FN": bias 7, max 448) to v >= 0, ties to even, saturating.

@@ -1,0 +1,83 @@
+// quant_lane.hpp -- the per-lane steps of the INT4 activation quantizer on gfx950, shared
+// by the activation kernel and the GEMM epilogue that quantizes the next layer's input.
+// A lane holds 32 consecutive channels of one row (one half of a 64-channel group): the
+// lane of one FP6 MFMA fragment of packed_layout.hpp.  The quantizer is defined as a
+// sequence of individually rounded fp32 operations (page "Hugging Face 把 Nunchaku 4-bit
+// Diffusion 接到 Diffusers", 技术细节 1 step 3): s = absmax / 7, q = rne(x_hat / s).
+#pragma once
+
+#include <stdint.h>
+
+namespace svdq {
+namespace lane {
+
+constexpr float kMinNormal = 1.17549435e-38f;
+
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+// The lane's 32 values in the order of the FP6 conversion: ev[i] is channel 2i (the low
+// bf16 of word i), od[i] channel 2i + 1 (the high bf16).
+struct Vals {
+    f32x16v ev, od;
+};
+
+// 32 floats -> 32 FP6 E2M3 fields (value / scale, field 2i from ev[i], 2i+1 from od[i]) in
+// six dwords, one v_cvt_scalef32_2xpk16_fp6_f32.  Written as asm with an early-clobber
+// result: the instruction reads its 32 source registers over several cycles, so its six
+// result registers must not overlap them (left to itself the compiler may place them there).
+__device__ __forceinline__ u32x6 cvt_fp6x32(const f32x16v& ev, const f32x16v& od, float scale) {
+    u32x6 r;
+    asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3"
+                 : "=&v"(r) : "v"(ev), "v"(od), "v"(scale));
+    return r;
+}
+
+__device__ __forceinline__ float absmax32(const Vals& v) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fmaxf(fabsf(v.ev[i]), fabsf(v.od[i])));
+    return a;
+}
+
+// rne(xh / s) for the lane's 32 values, in place, with the fp32 quotient correctly rounded
+// as the code's definition requires.  The quotient is estimated as xh * (1/s) (within 2^-22
+// relative of the correctly rounded one, i.e. < 2e-6 for |q| <= 8); only when an estimate
+// lies within 4e-6 of a half-integer can the correctly rounded quotient round differently,
+// and then the lane redoes all 32 with the exact division (smooth32 recomputes x_hat).
+// s = absmax / 7 bounds |xh / s| by 7 (up to rounding), so rne never leaves [-7, 7] and the
+// definition's clamp to [-8, 7] is the identity.  Codes come out as floats with +0 for 0.
+// s = 0 (an all-zero group) gives codes 0.
+__device__ __forceinline__ float rne_keep_d(f32x16v& v, int i, float rcp, float dmax) {
+#pragma clang fp contract(off)
+    const float y = v[i] * rcp;
+    const float d = y - __builtin_rintf(y);
+    v[i] = y - d;   // = rne(y) exactly, with +0 where it is zero
+    return fmaxf(dmax, fabsf(d));
+}
+
+// rne(xh / s) for the lane's 32 values in place (see rne_keep_d): `recompute` refills v with
+// the smoothed values when the exact division is needed.
+template <class Recompute>
+__device__ __forceinline__ void int4_codes32_exact(Vals& v, float s, Recompute&& recompute) {
+#pragma clang fp contract(off)
+    const bool zero = s == 0.0f;
+    const float rcp = zero ? 0.0f : 1.0f / s;
+    float dmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        dmax = rne_keep_d(v.ev, i, rcp, dmax);
+        dmax = rne_keep_d(v.od, i, rcp, dmax);
+    }
+    if (!zero && (dmax > 0.499996f || s < kMinNormal)) {
+        recompute();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            v.ev[i] = __builtin_rintf(v.ev[i] / s) + 0.0f;
+            v.od[i] = __builtin_rintf(v.od[i] / s) + 0.0f;
+        }
+    }
+}
+
+}  // namespace lane
+}  // namespace svdq

@@ -204,6 +204,34 @@ svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const vo
                                   const void* bias, int32_t act, int32_t out_dtype, void* out,
                                   svdq_stream_t stream);
 
+/* Two chained linears on the packed path with the second one's activation kernel fused into
+ * the first one's GEMM (the DiT MLP: fc1 with GELU, then fc2).  The pages credit the original
+ * engine's extra speed to such per-architecture fusions of the GELU/MLP kernels (page
+ * "Hugging Face 把 Nunchaku 4-bit Diffusion 接到 Diffusers", 技术细节 2; page "Diffusers
+ * integra Nunchaku ...", the section on why the original engine is still faster).  Same
+ * results as
+ *
+ *   svdq_gemm_w4a4_packed(cfg, M, act_packed, prepacked, lora_act, l2, bias, act,
+ *                         SVDQ_DT_BF16, h)
+ *   svdq_quantize_act_packed(next_cfg, M, h, next_smooth_inv, prepack(next_l1),
+ *                            next_act_packed, next_act_scales, next_lora_act)
+ *
+ * without the bf16 activations h [M, cfg->out_features] ever reaching memory: each output
+ * tile is quantized in the GEMM's epilogue from the bf16 values it would store.  Codes,
+ * scale words and next_act_scales are bit-identical to the unfused pair; next_lora_act
+ * (bf16 [M, next rank]) is the same sum in another fp32 order (within one bf16 ulp; the
+ * tiles' partial sums are added in no fixed order, so it is not bit-reproducible).
+ * next_cfg->in_features must equal cfg->out_features (both INT4).  next_l1 is the next
+ * layer's row-major bf16 [rank, K] factor (not prepacked); lora_workspace is caller-owned
+ * fp32 [M, next rank] scratch (overwritten).  next_act_scales may be NULL; next_l1,
+ * next_lora_act and lora_workspace may be NULL at next rank 0.  Enqueued on `stream`. */
+svdq_status svdq_gemm_w4a4_packed_quantize_next(
+    const svdq_layer_cfg* cfg, int64_t M, const void* act_packed, const void* prepacked,
+    const void* lora_act, const void* l2, const void* bias, int32_t act,
+    const svdq_layer_cfg* next_cfg, const float* next_smooth_inv, const void* next_l1,
+    void* next_act_packed, float* next_act_scales, void* next_lora_act, float* lora_workspace,
+    svdq_stream_t stream);
+
 /* LoRA adapters through the low-rank branch (page "Diffusers integra Nunchaku ...",
  * "Nunchaku Lite: integración y modelo de ejecución": LoRA keeps working because the module
  * structure is kept; page "Diffusers Natively Integrates Nunchaku Lite ...", the paragraph

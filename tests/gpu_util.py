@@ -246,3 +246,25 @@ def assert_lora_close(got_bits, oracle_bits, x_bf16, l1_bf16, min_exact=0.99):
     assert not bad.any(), f"{bad.sum()} lora_act elements beyond the fp32 error bound"
     frac = np.mean(np.asarray(got_bits) == np.asarray(oracle_bits))
     assert frac >= min_exact, f"only {frac:.4f} of lora_act equal to the oracle"
+
+
+def gemm_packed_quantize_next(apacked, wpacked, M, K, N, lora, l2, bias, act, next_si, next_l1,
+                              with_scales=True):
+    """svdq_gemm_w4a4_packed_quantize_next: the packed GEMM with the next layer's activation
+    kernel in its epilogue -> (next packed buffer, fp32 scales or None, next lora_act)."""
+    r = 0 if lora is None else lora.shape[1]
+    r2 = 0 if next_l1 is None else next_l1.shape[0]
+    cfg = bd.LayerCfg.make(K, N, r)
+    ncfg = bd.LayerCfg.make(N, 1, r2)
+    l2d = None if l2 is None or r == 0 else (l2 if torch.is_tensor(l2) else dev(l2))
+    bd_ = None if bias is None else (bias if torch.is_tensor(bias) else dev(bias))
+    lo = None if r == 0 else (lora if torch.is_tensor(lora) else dev(lora))
+    si = next_si if torch.is_tensor(next_si) else dev(np.asarray(next_si, np.float32))
+    l1d = None if r2 == 0 else (next_l1 if torch.is_tensor(next_l1) else dev(next_l1))
+    buf = torch.empty(act_packed_bytes(M, N), dtype=torch.uint8, device="cuda:0")
+    scales = empty((M, N // 64), np.float32) if with_scales else None
+    nlora = empty((M, r2), np.uint16) if r2 else None
+    work = empty((M, r2), np.float32) if r2 else None
+    bd.svdq_gemm_w4a4_packed_quantize_next(cfg, M, apacked, wpacked, lo, l2d, bd_, act, ncfg, si,
+                                           l1d, buf, scales, nlora, work)
+    return buf, scales, nlora

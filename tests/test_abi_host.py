@@ -150,6 +150,30 @@ def test_merge_lora_rank_rules():
                              FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
 
 
+def test_quantize_next_argument_rules():
+    """The fused MLP entry point rejects a next layer whose width is not this layer's output
+    width, a bad act code, a missing packed output and, at next rank > 0, a missing
+    workspace, before touching the device."""
+    L = bd.lib()
+    f = L.svdq_gemm_w4a4_packed_quantize_next
+    cfg = bd.LayerCfg.make(256, 384, 16)
+
+    def call(ncfg, act=1, packed=FAKE, work=FAKE, lora=FAKE):
+        return f(ctypes.byref(cfg), 300, FAKE, FAKE, FAKE, FAKE, FAKE, act, ctypes.byref(ncfg),
+                 FAKE, FAKE, packed, None, lora, work, None)
+
+    assert call(bd.LayerCfg.make(448, 1, 32)) == bd.SVDQ_ERR_INVALID_ARG
+    assert "in_features" in bd.svdq_last_error()
+    ok = bd.LayerCfg.make(384, 1, 32)
+    assert call(ok, act=2) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(ok, packed=None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "next_act_packed" in bd.svdq_last_error()
+    assert call(ok, work=None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "lora_workspace" in bd.svdq_last_error()
+    assert call(ok, lora=None) == bd.SVDQ_ERR_INVALID_ARG
+    assert call(bd.LayerCfg.make(384, 1, 32, "nvfp4")) == bd.SVDQ_ERR_UNSUPPORTED_CONFIG
+
+
 def test_python_binding_raises_with_message():
     cfg = bd.LayerCfg.make(100, 512, 16)
     with pytest.raises(bd.SvdqError) as e:
