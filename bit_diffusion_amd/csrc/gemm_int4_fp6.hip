@@ -141,6 +141,13 @@ constexpr int kStgStride = kBf16 ? 208 : 416;
 // The tile as bf16 in LDS for the next layer's quantization: [256 rows][192 columns], row
 // stride 400 bytes.
 constexpr int kTileStride = 2 * kBN + 16;
+// the next layer's operands beside the bf16 tile: l1 (up to rank 128) and smoothing slices
+constexpr int kMaxNextRank = 128;
+constexpr int kMaxL1Pieces = kMaxNextRank * 24 / kThreads;   // 16-byte pieces per thread
+constexpr int kL1SliceOff = kBM * kTileStride;
+constexpr int kSiSliceOff = kL1SliceOff + kMaxNextRank * kTileStride;
+static_assert(kMaxNextRank * 24 % kThreads == 0, "whole pieces per thread");
+static_assert(kSiSliceOff + 4 * kBN <= kSmemBytes, "the slices fit beside the tile");
 static_assert(kBM * kTileStride <= kSmemBytes, "the bf16 tile fits in the pipeline buffers");
 
 template <bool kBf16, bool kGelu, bool kNext = false>
@@ -432,8 +439,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         // (the tile's 192 columns are three whole groups), codes and scales in the packed
         // layout, and this tile's share of the next low-rank down-projection.
         static_assert(kBf16, "the next layer reads bf16");
+        const int G2 = N >> 6;                    // the next layer's groups
+        const int ngr = min(3, (N - n0) >> 6);    // whole groups in this tile
+        const int R2 = p.next_r;
+        const int tid = threadIdx.x;
+        // the tile's slices of the next layer's smoothing factors and l1 (rows of R2, this
+        // tile's channels), loaded into registers now so their latency overlaps the tile's
+        // store to LDS, and stored next to it after the barrier
+        const uint16_t* l1n = (const uint16_t*)p.next_l1;
+        const int nl1 = R2 * 24;                  // 16-byte pieces of the l1 slice
+        uint4 l1v[kMaxL1Pieces];
+#pragma unroll
+        for (int k = 0; k < kMaxL1Pieces; ++k) {
+            const int idx = tid + kThreads * k, jr = idx / 24, c8 = idx - 24 * jr;
+            l1v[k] = idx < nl1 && c8 < 8 * ngr
+                         ? *reinterpret_cast<const uint4*>(l1n + (int64_t)jr * N + n0 + 8 * c8)
+                         : make_uint4(0u, 0u, 0u, 0u);
+        }
+        const float4 siv = tid < 16 * ngr ? *reinterpret_cast<const float4*>(p.next_si + n0 + 4 * tid)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
         barrier();   // every wave is done with the pipeline buffers
         uint8_t* tl = smem;
+        uint8_t* l1t = smem + kL1SliceOff;
+        float* sil = reinterpret_cast<float*>(smem + kSiSliceOff);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -445,19 +473,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
                     *reinterpret_cast<uint16_t*>(tl + rr * kTileStride + 2 * cc) =
                         (uint16_t)f32_to_bf16(acc[i][j][e]);
                 }
+#pragma unroll
+        for (int k = 0; k < kMaxL1Pieces; ++k) {
+            const int idx = tid + kThreads * k, jr = idx / 24, c8 = idx - 24 * jr;
+            if (idx < nl1) *reinterpret_cast<uint4*>(l1t + jr * kTileStride + 16 * c8) = l1v[k];
+        }
+        if (tid < 48) *reinterpret_cast<float4*>(sil + 4 * tid) = siv;
         barrier();
-        const int G2 = N >> 6;                    // the next layer's groups
-        const int ngr = min(3, (N - n0) >> 6);    // whole groups in this tile
-        // 24 fragments (8 blocks of 32 rows x 3 groups); wave w quantizes w, w + 8, w + 16.
-        // Lane L: row L % 32 of the block, channels 32 (L / 32) .. + 31 of the group.
+        // 24 fragments (8 blocks of 32 rows x 3 groups); wave w quantizes rows 32 w .. + 31
+        // of each group.  Lane L: row L % 32 of the block, channels 32 (L / 32) .. + 31.
         const int h = lane >> 5, r32 = lane & 31;
+        const int rr = wave * 32 + r32;
+        const int64_t row = m0 + rr;
 #pragma unroll 1
-        for (int jb = 0; jb < 3; ++jb) {
-            const int job = wave + 8 * jb;
-            const int rb = job & 7, gi = job >> 3;
-            if (gi >= ngr) continue;
-            const int rr = rb * 32 + r32;
-            const int64_t row = m0 + rr;
+        for (int gi = 0; gi < ngr; ++gi) {
             const int c0 = gi * 64 + 32 * h;
             uint4 xw[4];
 #pragma unroll
@@ -465,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
                 xw[t] = row < M ? *reinterpret_cast<const uint4*>(tl + rr * kTileStride + 2 * (c0 + 8 * t))
                                 : make_uint4(0u, 0u, 0u, 0u);   // padding rows quantize to zero
             lane::Vals v;
-            const float* si = p.next_si + n0 + c0;
+            const float* si = sil + c0;
             auto smooth = [&] {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
@@ -495,31 +524,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
                 if (row < M && p.next_scales) p.next_scales[row * G2 + g2] = s;
             }
         }
-        // this tile's columns' share of the next layer's lora_act = x . l1^T: wave w takes
-        // rows 32 w .. + 31; the partial sums go into the zeroed fp32 workspace
-        const int R2 = p.next_r;
+        // this tile's channels' share of the next layer's lora_act = x . l1^T for rows
+        // 32 w .. + 31 (two 16-row MFMA blocks), added into the zeroed fp32 workspace
         if (R2 > 0) {
-            const uint16_t* l1n = (const uint16_t*)p.next_l1;
-            const int nks = (ngr * 64) >> 5;   // 32-channel steps
+            const int nks = 2 * ngr;   // 32-channel steps
+            uint4 av[2][6];
+#pragma unroll
+            for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+                for (int ks = 0; ks < 6; ++ks)
+                    if (ks < nks)
+                        av[rb2][ks] = *reinterpret_cast<const uint4*>(
+                            tl + (wave * 32 + rb2 * 16 + (lane & 15)) * kTileStride + 2 * (32 * ks + 8 * (lane >> 4)));
 #pragma unroll 1
-            for (int rb2 = 0; rb2 < 2; ++rb2) {
-                const int ar = wave * 32 + rb2 * 16 + (lane & 15);
-#pragma unroll 1
-                for (int jb = 0; jb < R2 / 16; ++jb) {
-                    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const uint16_t* brow = l1n + (int64_t)(16 * jb + (lane & 15)) * N + n0 + 8 * (lane >> 4);
-#pragma unroll 1
-                    for (int ks = 0; ks < nks; ++ks) {
-                        const uint4 av = *reinterpret_cast<const uint4*>(tl + ar * kTileStride + 2 * (32 * ks + 8 * (lane >> 4)));
-                        const uint4 bv4 = *reinterpret_cast<const uint4*>(brow + 32 * ks);
-                        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv4), c, 0, 0, 0);
+            for (int jb = 0; jb < R2 / 16; ++jb) {
+                f32x4 c[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+                const uint8_t* bl = l1t + (16 * jb + (lane & 15)) * kTileStride + 16 * (lane >> 4);
+#pragma unroll
+                for (int ks = 0; ks < 6; ++ks)
+                    if (ks < nks) {
+                        const uint4 bv4 = *reinterpret_cast<const uint4*>(bl + 64 * ks);
+#pragma unroll
+                        for (int rb2 = 0; rb2 < 2; ++rb2)
+                            c[rb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[rb2][ks]), as_bf16x8(bv4), c[rb2], 0, 0, 0);
                     }
 #pragma unroll
+                for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int64_t row = m0 + wave * 32 + rb2 * 16 + 4 * (lane >> 4) + i;
-                        if (row < M) unsafeAtomicAdd(p.lora_work + row * R2 + 16 * jb + (lane & 15), c[i]);
+                        const int64_t rw = m0 + wave * 32 + rb2 * 16 + 4 * (lane >> 4) + i;
+                        if (rw < M) unsafeAtomicAdd(p.lora_work + rw * R2 + 16 * jb + (lane & 15), c[rb2][i]);
                     }
-                }
             }
         }
         return;

@@ -3,7 +3,7 @@ kernel fused into fc1's GEMM epilogue: its packed codes, scale words and fp32 sc
 bit-identical to fc1's packed GEMM (bf16 out) followed by svdq_quantize_act_packed, and
 its lora_act is within the fp32 summation bound of the oracle's down-projection of the
 same bf16 intermediate.  Shapes cover ragged token counts, fc1 widths that end in a
-partial 192-column tile, GELU on and off, next ranks 0 to 48, and the MLP end to end
+partial 192-column tile, GELU on and off, next ranks 0 to 128, and the MLP end to end
 against the oracle chain."""
 import numpy as np
 import pytest
@@ -35,6 +35,8 @@ def _fc1(rng, M, K1, N1, r1):
     (64, 128, 192, 16, 0, 1),       # next rank 0: no down-projection
     (1000, 256, 1344, 32, 48, 1),   # seven column tiles, rank 48
     (1, 128, 576, 16, 16, 1),       # a single token
+    (300, 128, 384, 16, 128, 1),    # the maximum next rank
+    (260, 192, 448, 16, 128, 0),    # maximum rank with a partial last column tile
 ])
 def test_fused_matches_unfused(M, K1, N1, r1, r2, act):
     rng = np.random.default_rng(1500 + M + N1 + r2)
