@@ -294,6 +294,47 @@ def mlp_leg(steps, sp, stream):
             "fused_vs_unfused_rel": float(f"{fused_rel:.3e}")}
 
 
+def weights_leg(steps, sp, stream):
+    """Offline weight quantization of the attention projection (N = K = 3072, rank 32):
+    calibration absmax over 4096 bf16 tokens, smoothing factors from an fp32 weight, and the
+    INT4 residual given bf16 top-r factors (the factorization itself is the caller's SVD).
+    Algorithmic bytes: calibration reads x; smoothing reads w; the residual reads w, l1,
+    l2, smooth_inv and writes the codes and scales."""
+    import torch
+    import bit_diffusion_amd as bd
+    Mc, K, N, Rw = 4096, 3072, 3072, 32
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(41)
+    x = (torch.randn((Mc, K), device=dev, generator=g)).to(torch.bfloat16).view(torch.int16)
+    w = torch.randn((N, K), device=dev, generator=g) * 0.02
+    l1 = (torch.randn((Rw, K), device=dev, generator=g) * 0.05).to(torch.bfloat16).view(torch.int16)
+    l2 = (torch.randn((N, Rw), device=dev, generator=g) * 0.05).to(torch.bfloat16).view(torch.int16)
+    cfg = bd.LayerCfg.make(K, N, Rw)
+    am = torch.zeros(K, dtype=torch.float32, device=dev)
+    wam = torch.empty(K, dtype=torch.float32, device=dev)
+    si = torch.empty(K, dtype=torch.float32, device=dev)
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // 64), dtype=torch.float32, device=dev)
+    calib = lambda i: bd.svdq_calib_absmax(Mc, K, x, am, sp)
+    smooth = lambda i: bd.svdq_smoothing_factors(cfg, w, am, wam, si, sp)
+    resid = lambda i: bd.svdq_quantize_residual(cfg, w, si, l1, l2, codes, scales, sp)
+    for f in (calib, smooth, resid):
+        f(0)
+    torch.cuda.synchronize()
+    n = max(5, steps // 5)
+    ms_c, ms_s, ms_r = (time_launches(f, n, stream) for f in (calib, smooth, resid))
+    b_c = Mc * K * 2 + K * 4
+    b_s = N * K * 4 + 3 * K * 4
+    b_r = N * K * 4 + Rw * K * 2 + N * Rw * 2 + K * 4 + N * K // 2 + N * (K // 64) * 4
+    fp64 = 2.0 * N * K * Rw
+    return {"workload": "weights_3072x3072_r32_calib4096",
+            "calib_absmax_ms": round(ms_c, 4), "calib_absmax_GBs": round(b_c / (ms_c * 1e-3) / 1e9, 1),
+            "smoothing_factors_ms": round(ms_s, 4), "smoothing_factors_GBs": round(b_s / (ms_s * 1e-3) / 1e9, 1),
+            "quantize_residual_ms": round(ms_r, 4), "quantize_residual_GBs": round(b_r / (ms_r * 1e-3) / 1e9, 1),
+            "quantize_residual_fp64_TFLOPs": round(fp64 / (ms_r * 1e-3) / 1e12, 2)}
+
+
 def lora_leg(steps, sp, stream, si, sets):
     """The attention projection with a rank-16 LoRA adapter merged into its low-rank branch
     (svdq_merge_lora: rank 32 + 16 = 48), eager launches over the same rotating inputs."""
@@ -536,6 +577,7 @@ def main():
         out["nvfp4"] = nvfp4_leg(args.steps, sp, stream)
         out["mlp"] = mlp_leg(args.steps, sp, stream)
         out["lora"] = lora_leg(args.steps, sp, stream, si, sets)
+        out["weights"] = weights_leg(args.steps, sp, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     print(json.dumps(out), flush=True)

@@ -20,7 +20,8 @@ __all__ = [
     "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
     "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
     "svdq_prepacked_l1_bytes", "svdq_prepack_l1", "svdq_merged_rank", "svdq_merge_lora",
-    "svdq_gemm_w4a4_packed_quantize_next",
+    "svdq_gemm_w4a4_packed_quantize_next", "svdq_calib_absmax", "svdq_smoothing_factors",
+    "svdq_quantize_residual",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -141,6 +142,21 @@ def svdq_gemm_w4a4_packed_quantize_next(cfg, M, act_packed, prepacked, lora_act,
         _ptr(bias), int(act), ctypes.byref(next_cfg), _ptr(next_smooth_inv), _ptr(next_l1),
         _ptr(next_act_packed), _ptr(next_act_scales), _ptr(next_lora_act), _ptr(lora_workspace),
         _stream(stream)))
+
+
+def svdq_calib_absmax(M, K, x, absmax, stream=None):
+    return _check(lib().svdq_calib_absmax(int(M), int(K), _ptr(x), _ptr(absmax), _stream(stream)))
+
+
+def svdq_smoothing_factors(cfg, w, x_absmax, w_absmax, smooth_inv, stream=None):
+    return _check(lib().svdq_smoothing_factors(ctypes.byref(cfg), _ptr(w), _ptr(x_absmax),
+                                               _ptr(w_absmax), _ptr(smooth_inv), _stream(stream)))
+
+
+def svdq_quantize_residual(cfg, w, smooth_inv, l1, l2, wgt_codes, wgt_scales, stream=None):
+    return _check(lib().svdq_quantize_residual(ctypes.byref(cfg), _ptr(w), _ptr(smooth_inv),
+                                               _ptr(l1), _ptr(l2), _ptr(wgt_codes), _ptr(wgt_scales),
+                                               _stream(stream)))
 
 
 def svdq_check_device(device=0):

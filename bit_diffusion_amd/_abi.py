@@ -27,7 +27,8 @@ EXPORTS = ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_
            "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
            "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
            "svdq_prepacked_l1_bytes", "svdq_prepack_l1", "svdq_merged_rank", "svdq_merge_lora",
-           "svdq_gemm_w4a4_packed_quantize_next")
+           "svdq_gemm_w4a4_packed_quantize_next", "svdq_calib_absmax", "svdq_smoothing_factors",
+           "svdq_quantize_residual")
 
 
 class LayerCfg(ctypes.Structure):
@@ -78,6 +79,9 @@ def lib():
         L.svdq_merge_lora.argtypes = [cfgp, I32, P, P, P, P, F, P, P, P]
         L.svdq_gemm_w4a4_packed_quantize_next.argtypes = [cfgp, I64, P, P, P, P, P, I32, cfgp, P, P,
                                                            P, P, P, P, P]
+        L.svdq_calib_absmax.argtypes = [I64, I32, P, P, P]
+        L.svdq_smoothing_factors.argtypes = [cfgp, P, P, P, P, P]
+        L.svdq_quantize_residual.argtypes = [cfgp, P, P, P, P, P, P, P]
         L.svdq_gemm_w4a4_packed.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P]
         L.svdq_check_device.argtypes = [ctypes.c_int]
         L.svdq_check_arch.argtypes = [ctypes.c_char_p]
@@ -90,7 +94,8 @@ def lib():
                      "svdq_check_device", "svdq_check_arch", "svdq_act_packed_bytes",
                      "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed", "svdq_pack_act",
                      "svdq_prepack_weight", "svdq_gemm_w4a4_packed", "svdq_prepacked_l1_bytes",
-                     "svdq_prepack_l1", "svdq_merge_lora", "svdq_gemm_w4a4_packed_quantize_next"):
+                     "svdq_prepack_l1", "svdq_merge_lora", "svdq_gemm_w4a4_packed_quantize_next",
+                     "svdq_calib_absmax", "svdq_smoothing_factors", "svdq_quantize_residual"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

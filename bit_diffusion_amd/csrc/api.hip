@@ -422,6 +422,57 @@ svdq_status svdq_gemm_w4a4_packed_quantize_next(
     return after_launch("svdq_gemm_w4a4_packed_quantize_next");
 }
 
+svdq_status svdq_calib_absmax(int64_t M, int32_t K, const void* x, float* absmax,
+                              svdq_stream_t stream) {
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    if (K <= 0 || K % 64 != 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "K = %d must be a positive multiple of 64", K);
+    if (M > 0) SVDQ_TRY(check_ptr(x, "x", 16));
+    SVDQ_TRY(check_ptr(absmax, "absmax", 16));
+    if ((M + 31) / 32 >= 65536)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
+    SVDQ_TRY(check_current_device());
+    if (M == 0) return SVDQ_OK;
+    svdq::launch_calib_absmax(M, K, x, absmax, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_calib_absmax");
+}
+
+svdq_status svdq_smoothing_factors(const svdq_layer_cfg* cfg, const float* w, const float* x_absmax,
+                                   float* w_absmax, float* smooth_inv, svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_ptr(w, "w", 16));
+    SVDQ_TRY(check_ptr(x_absmax, "x_absmax", 4));
+    SVDQ_TRY(check_ptr(w_absmax, "w_absmax", 16));
+    SVDQ_TRY(check_ptr(smooth_inv, "smooth_inv", 4));
+    if ((cfg->out_features + 31) / 32 >= 65536)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "out_features %d too large for one launch", cfg->out_features);
+    SVDQ_TRY(check_current_device());
+    svdq::launch_smoothing_factors(cfg->out_features, cfg->in_features, w, x_absmax, w_absmax,
+                                   smooth_inv, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_smoothing_factors");
+}
+
+svdq_status svdq_quantize_residual(const svdq_layer_cfg* cfg, const float* w, const float* smooth_inv,
+                                   const void* l1, const void* l2, void* wgt_codes, float* wgt_scales,
+                                   svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    SVDQ_TRY(check_ptr(w, "w", 16));
+    SVDQ_TRY(check_ptr(smooth_inv, "smooth_inv", 16));
+    if (cfg->rank > 0) {
+        SVDQ_TRY(check_ptr(l1, "l1", 16));
+        SVDQ_TRY(check_ptr(l2, "l2", 2));
+    }
+    SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", 16));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", 4));
+    if ((int64_t)cfg->out_features * (cfg->in_features / 32) / 256 >= ((int64_t)1 << 31))
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "layer too large for one launch");
+    SVDQ_TRY(check_current_device());
+    svdq::launch_quantize_residual(cfg->out_features, cfg->in_features, cfg->rank, w, smooth_inv, l1,
+                                   l2, wgt_codes, wgt_scales, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_quantize_residual");
+}
+
 svdq_status svdq_check_device(int device) { return check_device_ordinal(device); }
 
 svdq_status svdq_check_arch(const char* arch_name) {

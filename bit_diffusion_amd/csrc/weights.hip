@@ -1,0 +1,182 @@
+// weights.hip -- the offline weight side of SVDQuant on gfx950 (page "Hugging Face 把 Nunchaku
+// 4-bit Diffusion 接到 Diffusers", 技术细节 1, "SVDQuant 的核心思路" and the quantize-your-own-
+// model walk-through; page "Diffusers integra Nunchaku ...", the section on quantizing a model
+// with diffuse-compressor): calibration absmax, per-channel smoothing factors, and the 4-bit
+// residual of the smoothed weight once the 16-bit low-rank branch is taken out.  All three are
+// HBM-bound elementwise or column reductions; the residual's low-rank product runs in fp64 so
+// that the residual, and with it every code and scale, is the exact result of its definition.
+#include "common.hpp"
+#include "launch.hpp"
+#include "quant_lane.hpp"
+
+namespace svdq {
+namespace {
+
+constexpr int kColThreads = 256, kColRows = 32;   // column pieces per block, rows per block
+
+// out[c] = max(out[c], max over this block's rows of |x[r, c]|) for bf16 x [M, K], 8 columns
+// per thread.  |x| as fp32 bits: non-negative floats order like their bit patterns (a NaN
+// ranks above every number, so it survives the max as it does in the definition's max).
+__global__ __launch_bounds__(kColThreads) void col_absmax_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                      int64_t M, int K,
+                                                                      unsigned* __restrict__ out) {
+    const int c8 = blockIdx.x * kColThreads + threadIdx.x;
+    if (8 * c8 >= K) return;
+    const int64_t r0 = (int64_t)blockIdx.y * kColRows, r1 = min(M, r0 + kColRows);
+    uint32_t m[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll 8
+    for (int64_t r = r0; r < r1; ++r) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + r * K + 8 * c8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[2 * i] = max(m[2 * i], (w[i] & 0x7FFFu) << 16);
+            m[2 * i + 1] = max(m[2 * i + 1], w[i] & 0x7FFF0000u);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) atomicMax(out + 8 * c8 + i, m[i]);
+}
+
+// the same over fp32 w [N, K], 4 columns per thread
+__global__ __launch_bounds__(kColThreads) void col_absmax_f32_kernel(const float* __restrict__ w,
+                                                                     int64_t N, int K,
+                                                                     unsigned* __restrict__ out) {
+    const int c4 = blockIdx.x * kColThreads + threadIdx.x;
+    if (4 * c4 >= K) return;
+    const int64_t r0 = (int64_t)blockIdx.y * kColRows, r1 = min(N, r0 + kColRows);
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 8
+    for (int64_t r = r0; r < r1; ++r) {
+        const uint4 v = *reinterpret_cast<const uint4*>(w + r * K + 4 * c4);
+        m[0] = max(m[0], v.x & 0x7FFFFFFFu);
+        m[1] = max(m[1], v.y & 0x7FFFFFFFu);
+        m[2] = max(m[2], v.z & 0x7FFFFFFFu);
+        m[3] = max(m[3], v.w & 0x7FFFFFFFu);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) atomicMax(out + 4 * c4 + i, m[i]);
+}
+
+__global__ __launch_bounds__(256) void fill_zero_u32_kernel(unsigned* __restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Smoothing factor of channel k, migrating activation outliers into the weight (技术细节 1
+// step 1): lambda = sqrt(cx / cw) in binary64 (1 where it is not a positive finite number or
+// either maximum is 0), stored as smooth_inv = fp32(1 / lambda).  Each operation is one
+// correctly rounded binary64 operation, so the result is a function of (cx, cw) alone.
+__global__ __launch_bounds__(256) void smooth_factor_kernel(const float* __restrict__ cx,
+                                                            const float* __restrict__ cw, int K,
+                                                            float* __restrict__ smooth_inv) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= K) return;
+    const double a = cx[k], b = cw[k];
+    double lam = __builtin_sqrt(a / b);
+    if (!__builtin_isfinite(lam) || lam == 0.0 || a == 0.0 || b == 0.0) lam = 1.0;
+    smooth_inv[k] = (float)(1.0 / lam);
+}
+
+// The 4-bit residual of one layer (技术细节 1 steps 2 and 3).  With lam_k = 1 / smooth_inv[k]
+// (binary64), the smoothed weight is w_hat = w lam_k; the low-rank branch carries
+// (l2 l1)[n, k] lam_k (l1 absorbs smooth_inv, so un-smoothing it gives the branch's share of
+// w_hat); the residual R = fp32(w_hat - (l2 l1) lam) is quantized per 64-channel group with the
+// activation rule (s = absmax / 7, q = rne(R / s)).  (l2 l1)[n, k] sums r products of two bf16
+// values: each product is exact in binary64 and so is their sum (while the r products span
+// fewer than 2^37 in magnitude), so no summation order changes it.  Thread t: row
+// t / (K / 32), channels 32 (t % (K / 32)) .. + 31; the lanes t, t ^ 1 share a group.
+__global__ __launch_bounds__(256) void residual_int4_kernel(const float* __restrict__ w,
+                                                            const float* __restrict__ smooth_inv,
+                                                            const uint16_t* __restrict__ l1,
+                                                            const uint16_t* __restrict__ l2, int N,
+                                                            int K, int r,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+#pragma clang fp contract(off)
+    const int hpr = K >> 5;   // 32-channel halves per row (even)
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)N * hpr) return;   // whole pairs: N * hpr is even
+    const int n = (int)(t / hpr), hg = (int)(t - (int64_t)n * hpr), c0 = 32 * hg;
+    double p[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) p[c] = 0.0;
+    for (int j = 0; j < r; ++j) {
+        const double u = (double)__uint_as_float((uint32_t)l2[(int64_t)n * r + j] << 16);
+        const uint4* lr = reinterpret_cast<const uint4*>(l1 + (int64_t)j * K + c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = lr[q];
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[8 * q + 2 * i] = __builtin_fma(u, (double)__uint_as_float(wd[i] << 16), p[8 * q + 2 * i]);
+                p[8 * q + 2 * i + 1] =
+                    __builtin_fma(u, (double)__uint_as_float(wd[i] & 0xFFFF0000u), p[8 * q + 2 * i + 1]);
+            }
+        }
+    }
+    lane::Vals v, keep;
+    const float4* wr = reinterpret_cast<const float4*>(w + (int64_t)n * K + c0);
+    const float4* sr = reinterpret_cast<const float4*>(smooth_inv + c0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float4 wv = wr[q], sv = sr[q];
+        const float wf[4] = {wv.x, wv.y, wv.z, wv.w}, sf[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * q + i;
+            const double lam = 1.0 / (double)sf[i];
+            const double wh = (double)wf[i] * lam;
+            const float rv = r > 0 ? (float)(wh - p[c] * lam) : (float)wh;
+            if (c & 1) keep.od[c >> 1] = rv;
+            else keep.ev[c >> 1] = rv;
+        }
+    }
+    v = keep;
+    float a = lane::absmax32(v);
+    a = fmaxf(a, __shfl_xor(a, 1, 64));   // the group's other half
+    const float s = a / 7.0f;
+    lane::int4_codes32_exact(v, s, [&] { v = keep; });
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t pair = ((uint32_t)(int)v.ev[i] & 15u) | (((uint32_t)(int)v.od[i] & 15u) << 4);
+        d[i >> 2] |= pair << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint4*>(codes + (int64_t)n * (K / 2) + 16 * hg) = make_uint4(d[0], d[1], d[2], d[3]);
+    if ((hg & 1) == 0) scales[(int64_t)n * (K / 64) + (hg >> 1)] = s;
+}
+
+dim3 col_grid(int64_t rows, int K, int per_thread) {
+    const int pieces = K / per_thread;
+    return dim3((unsigned)((pieces + kColThreads - 1) / kColThreads), (unsigned)((rows + kColRows - 1) / kColRows));
+}
+
+}  // namespace
+
+void launch_calib_absmax(int64_t M, int K, const void* x, float* absmax, hipStream_t st) {
+    hipLaunchKernelGGL(col_absmax_bf16_kernel, col_grid(M, K, 8), dim3(kColThreads), 0, st,
+                       (const uint16_t*)x, M, K, reinterpret_cast<unsigned*>(absmax));
+}
+
+void launch_smoothing_factors(int N, int K, const float* w, const float* x_absmax, float* w_absmax,
+                              float* smooth_inv, hipStream_t st) {
+    hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<unsigned*>(w_absmax), K);
+    hipLaunchKernelGGL(col_absmax_f32_kernel, col_grid(N, K, 4), dim3(kColThreads), 0, st, w,
+                       (int64_t)N, K, reinterpret_cast<unsigned*>(w_absmax));
+    hipLaunchKernelGGL(smooth_factor_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st,
+                       x_absmax, (const float*)w_absmax, K, smooth_inv);
+}
+
+void launch_quantize_residual(int N, int K, int r, const float* w, const float* smooth_inv,
+                              const void* l1, const void* l2, void* codes, float* scales,
+                              hipStream_t st) {
+    const int64_t threads = (int64_t)N * (K / 32);
+    hipLaunchKernelGGL(residual_int4_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, w,
+                       smooth_inv, (const uint16_t*)l1, (const uint16_t*)l2, N, K, r, (uint8_t*)codes,
+                       scales);
+}
+
+}  // namespace svdq

@@ -232,6 +232,39 @@ svdq_status svdq_gemm_w4a4_packed_quantize_next(
     void* next_act_packed, float* next_act_scales, void* next_lora_act, float* lora_workspace,
     svdq_stream_t stream);
 
+/* Offline weight quantization: the calibrate-and-quantize step that turns a layer's weight
+ * into the tensors the kernels above consume (page "Hugging Face 把 Nunchaku 4-bit Diffusion
+ * 接到 Diffusers", 技术细节 1 "SVDQuant 的核心思路" steps 1-3 and its quantize-your-own-model
+ * walk-through; page "Diffusers integra Nunchaku ...", the diffuse-compressor section).  The
+ * pages give no formulas; the readings are:
+ *
+ * svdq_calib_absmax: absmax[k] = max(absmax[k], max_m |x[m, k]|) over bf16 calibration
+ *   activations x [M, K] (K a multiple of 64); call once per batch on an absmax first
+ *   filled with zeros.  Exact.
+ * svdq_smoothing_factors: per input channel k of the fp32 weight w [N, K] (N = out_features),
+ *   cw[k] = max_n |w[n, k]| (written to w_absmax, fp32 [K], caller-owned) and the smoothing
+ *   factor lambda = sqrt(x_absmax[k] / cw[k]) in binary64, 1 where it is not a positive
+ *   finite number or either maximum is 0; writes smooth_inv[k] = fp32(1 / lambda), the
+ *   activation kernel's input.  Exact given the maxima (correctly rounded binary64 steps).
+ * svdq_quantize_residual (INT4): with lam = 1 / smooth_inv (binary64), the 4-bit residual
+ *   R = fp32(w lam - (l2 l1) lam) of the smoothed weight once the low-rank branch (l1 bf16
+ *   [rank, K] with smooth_inv absorbed, l2 bf16 [N, rank], the same factors the GEMM and
+ *   the activation kernel take; may be NULL at rank 0) is taken out, quantized per
+ *   64-channel group like the activations: wgt_codes [N, K/2] nibbles and wgt_scales
+ *   [N, K/64] fp32, svdq_prepack_weight's inputs.  The low-rank product sums bf16 products
+ *   in binary64, exact while each element's products span less than 2^37, so the codes and
+ *   scales are those of the definition bit for bit.
+ * The top-r factorization between the two (the branch's l1, l2 from the smoothed weight's
+ * leading singular triplets) is a dense SVD left to the caller's linear-algebra library.
+ * All buffers are device memory owned by the caller; all enqueue on `stream`. */
+svdq_status svdq_calib_absmax(int64_t M, int32_t K, const void* x, float* absmax,
+                              svdq_stream_t stream);
+svdq_status svdq_smoothing_factors(const svdq_layer_cfg* cfg, const float* w, const float* x_absmax,
+                                   float* w_absmax, float* smooth_inv, svdq_stream_t stream);
+svdq_status svdq_quantize_residual(const svdq_layer_cfg* cfg, const float* w, const float* smooth_inv,
+                                   const void* l1, const void* l2, void* wgt_codes, float* wgt_scales,
+                                   svdq_stream_t stream);
+
 /* LoRA adapters through the low-rank branch (page "Diffusers integra Nunchaku ...",
  * "Nunchaku Lite: integración y modelo de ejecución": LoRA keeps working because the module
  * structure is kept; page "Diffusers Natively Integrates Nunchaku Lite ...", the paragraph

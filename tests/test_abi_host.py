@@ -174,6 +174,22 @@ def test_quantize_next_argument_rules():
     assert call(bd.LayerCfg.make(384, 1, 32, "nvfp4")) == bd.SVDQ_ERR_UNSUPPORTED_CONFIG
 
 
+def test_weight_quantizer_argument_rules():
+    L = bd.lib()
+    assert L.svdq_calib_absmax(10, 100, FAKE, FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_calib_absmax(-1, 128, FAKE, FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_calib_absmax(10, 128, None, FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
+    cfg = bd.LayerCfg.make(256, 128, 16)
+    assert L.svdq_smoothing_factors(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "w_absmax" in bd.svdq_last_error()
+    assert L.svdq_quantize_residual(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                    None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "l1" in bd.svdq_last_error()
+    nv = bd.LayerCfg.make(256, 128, 16, "nvfp4")
+    assert L.svdq_quantize_residual(ctypes.byref(nv), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    None) == bd.SVDQ_ERR_UNSUPPORTED_CONFIG
+
+
 def test_python_binding_raises_with_message():
     cfg = bd.LayerCfg.make(100, 512, 16)
     with pytest.raises(bd.SvdqError) as e:
