@@ -318,7 +318,7 @@ def weights_leg(steps, sp, stream):
     scales = torch.empty((N, K // 64), dtype=torch.float32, device=dev)
     calib = lambda i: bd.svdq_calib_absmax(Mc, K, x, am, sp)
     smooth = lambda i: bd.svdq_smoothing_factors(cfg, w, am, wam, si, sp)
-    resid = lambda i: bd.svdq_quantize_residual(cfg, w, si, l1, l2, codes, scales, sp)
+    resid = lambda i: bd.svdq_quantize_residual(cfg, w, si, l1, l2, codes, scales, None, sp)
     for f in (calib, smooth, resid):
         f(0)
     torch.cuda.synchronize()

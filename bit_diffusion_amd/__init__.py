@@ -153,10 +153,11 @@ def svdq_smoothing_factors(cfg, w, x_absmax, w_absmax, smooth_inv, stream=None):
                                                _ptr(w_absmax), _ptr(smooth_inv), _stream(stream)))
 
 
-def svdq_quantize_residual(cfg, w, smooth_inv, l1, l2, wgt_codes, wgt_scales, stream=None):
+def svdq_quantize_residual(cfg, w, smooth_inv, l1, l2, wgt_codes, wgt_scales, wgt_global_scale=None,
+                           stream=None):
     return _check(lib().svdq_quantize_residual(ctypes.byref(cfg), _ptr(w), _ptr(smooth_inv),
                                                _ptr(l1), _ptr(l2), _ptr(wgt_codes), _ptr(wgt_scales),
-                                               _stream(stream)))
+                                               _ptr(wgt_global_scale), _stream(stream)))
 
 
 def svdq_check_device(device=0):

@@ -81,7 +81,7 @@ def lib():
                                                            P, P, P, P, P]
         L.svdq_calib_absmax.argtypes = [I64, I32, P, P, P]
         L.svdq_smoothing_factors.argtypes = [cfgp, P, P, P, P, P]
-        L.svdq_quantize_residual.argtypes = [cfgp, P, P, P, P, P, P, P]
+        L.svdq_quantize_residual.argtypes = [cfgp, P, P, P, P, P, P, P, P]
         L.svdq_gemm_w4a4_packed.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P]
         L.svdq_check_device.argtypes = [ctypes.c_int]
         L.svdq_check_arch.argtypes = [ctypes.c_char_p]

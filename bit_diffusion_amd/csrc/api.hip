@@ -453,10 +453,10 @@ svdq_status svdq_smoothing_factors(const svdq_layer_cfg* cfg, const float* w, co
 }
 
 svdq_status svdq_quantize_residual(const svdq_layer_cfg* cfg, const float* w, const float* smooth_inv,
-                                   const void* l1, const void* l2, void* wgt_codes, float* wgt_scales,
-                                   svdq_stream_t stream) {
+                                   const void* l1, const void* l2, void* wgt_codes, void* wgt_scales,
+                                   float* wgt_global_scale, svdq_stream_t stream) {
     SVDQ_TRY(check_cfg(cfg));
-    SVDQ_TRY(check_int4(cfg));
+    const bool nv = cfg->precision == SVDQ_PREC_NVFP4;
     SVDQ_TRY(check_ptr(w, "w", 16));
     SVDQ_TRY(check_ptr(smooth_inv, "smooth_inv", 16));
     if (cfg->rank > 0) {
@@ -464,12 +464,14 @@ svdq_status svdq_quantize_residual(const svdq_layer_cfg* cfg, const float* w, co
         SVDQ_TRY(check_ptr(l2, "l2", 2));
     }
     SVDQ_TRY(check_ptr(wgt_codes, "wgt_codes", 16));
-    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", 4));
+    SVDQ_TRY(check_ptr(wgt_scales, "wgt_scales", nv ? 2 : 4));
+    if (nv) SVDQ_TRY(check_ptr(wgt_global_scale, "wgt_global_scale", 4));
     if ((int64_t)cfg->out_features * (cfg->in_features / 32) / 256 >= ((int64_t)1 << 31))
         return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "layer too large for one launch");
     SVDQ_TRY(check_current_device());
-    svdq::launch_quantize_residual(cfg->out_features, cfg->in_features, cfg->rank, w, smooth_inv, l1,
-                                   l2, wgt_codes, wgt_scales, reinterpret_cast<hipStream_t>(stream));
+    svdq::launch_quantize_residual(cfg->out_features, cfg->in_features, cfg->rank, nv, w, smooth_inv,
+                                   l1, l2, wgt_codes, wgt_scales, wgt_global_scale,
+                                   reinterpret_cast<hipStream_t>(stream));
     return after_launch("svdq_quantize_residual");
 }
 

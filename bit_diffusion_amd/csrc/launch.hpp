@@ -94,8 +94,8 @@ void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st);
 void launch_calib_absmax(int64_t M, int K, const void* x, float* absmax, hipStream_t st);
 void launch_smoothing_factors(int N, int K, const float* w, const float* x_absmax, float* w_absmax,
                               float* smooth_inv, hipStream_t st);
-void launch_quantize_residual(int N, int K, int r, const float* w, const float* smooth_inv,
-                              const void* l1, const void* l2, void* codes, float* scales,
-                              hipStream_t st);
+void launch_quantize_residual(int N, int K, int r, bool nvfp4, const float* w,
+                              const float* smooth_inv, const void* l1, const void* l2, void* codes,
+                              void* scales, float* global_scale, hipStream_t st);
 
 }  // namespace svdq

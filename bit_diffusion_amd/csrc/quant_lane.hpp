@@ -79,5 +79,59 @@ __device__ __forceinline__ void int4_codes32_exact(Vals& v, float s, Recompute&&
     }
 }
 
+// Nearest E4M3 ("FN": bias 7, max 448) to v >= 0, ties to even, saturating.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    if (!(v > 0.0f)) return 0u;
+    if (v >= 448.0f) return 0x7Eu;
+    uint32_t u = __float_as_uint(v);
+    int e = (int)(u >> 23) - 127;
+    if (e < -6) return (uint32_t)__builtin_rintf(v * 512.0f);   // subnormal, 2^-9 steps
+    u = u + 0x7FFFFu + ((u >> 20) & 1u);                          // round to 3 mantissa bits
+    u &= 0xFFF00000u;
+    int er = (int)(u >> 23) - 127;
+    return ((uint32_t)(er + 7) << 3) | ((u >> 20) & 7u);
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 0u) return (float)m * 0.001953125f;
+    return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Nearest E2M1 magnitude (0, .5, 1, 1.5, 2, 3, 4, 6), ties to the even code, saturating;
+// sign in bit 3.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+    float a = fabsf(v);
+    uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+               : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// NVFP4 for the lane's 32 values: two blocks of 16 (channels 0-15 are ev/od 0-7), each with
+// the E4M3 scale sb = e4m3(absmax / (6 S)) and E2M1 codes of v / (e4m3_decode(sb) S) (all
+// zero where sb is 0).  d: the 16 code bytes, low nibble the even channel; sbs: the two
+// scale bytes (block 0 in the low byte).
+__device__ __forceinline__ void nvfp4_codes32(const Vals& v, float S, uint32_t (&d)[4], uint32_t& sbs) {
+    const float den = 6.0f * S;
+    d[0] = d[1] = d[2] = d[3] = 0u;
+    sbs = 0u;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 8 * b; i < 8 * b + 8; ++i) a = fmaxf(a, fmaxf(fabsf(v.ev[i]), fabsf(v.od[i])));
+        const uint32_t sb = e4m3_encode(a / den);
+        sbs |= sb << (8 * b);
+        if (sb != 0u) {
+            const float dq = e4m3_decode(sb) * S;
+#pragma unroll
+            for (int i = 8 * b; i < 8 * b + 8; ++i) {
+                const uint32_t pair = e2m1_encode(v.ev[i] / dq) | (e2m1_encode(v.od[i] / dq) << 4);
+                d[i >> 2] |= pair << (8 * (i & 3));
+            }
+        }
+    }
+}
+
 }  // namespace lane
 }  // namespace svdq

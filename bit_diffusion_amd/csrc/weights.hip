@@ -81,29 +81,30 @@ __global__ __launch_bounds__(256) void smooth_factor_kernel(const float* __restr
 // The 4-bit residual of one layer (技术细节 1 steps 2 and 3).  With lam_k = 1 / smooth_inv[k]
 // (binary64), the smoothed weight is w_hat = w lam_k; the low-rank branch carries
 // (l2 l1)[n, k] lam_k (l1 absorbs smooth_inv, so un-smoothing it gives the branch's share of
-// w_hat); the residual R = fp32(w_hat - (l2 l1) lam) is quantized per 64-channel group with the
-// activation rule (s = absmax / 7, q = rne(R / s)).  (l2 l1)[n, k] sums r products of two bf16
-// values: each product is exact in binary64 and so is their sum (while the r products span
-// fewer than 2^37 in magnitude), so no summation order changes it.  Thread t: row
-// t / (K / 32), channels 32 (t % (K / 32)) .. + 31; the lanes t, t ^ 1 share a group.
-__global__ __launch_bounds__(256) void residual_int4_kernel(const float* __restrict__ w,
-                                                            const float* __restrict__ smooth_inv,
-                                                            const uint16_t* __restrict__ l1,
-                                                            const uint16_t* __restrict__ l2, int N,
-                                                            int K, int r,
-                                                            uint8_t* __restrict__ codes,
-                                                            float* __restrict__ scales) {
+// w_hat); the residual is R = fp32(w_hat - (l2 l1) lam).  (l2 l1)[n, k] sums r products of
+// two bf16 values: each product is exact in binary64 and so is their sum (while the r
+// products span fewer than 2^37 in magnitude), so no summation order changes it.  Thread t:
+// row t / (K / 32), channels 32 (t % (K / 32)) .. + 31; the lanes t, t ^ 1 share a 64-group.
+struct ResidualArgs {
+    const float* w;
+    const float* smooth_inv;
+    const uint16_t* l1;
+    const uint16_t* l2;
+    int N, K, r;
+    uint8_t* codes;
+    void* scales;
+    unsigned* gmax;   // NVFP4: the residual's max |R| (fp32 bits), then S_w
+};
+
+__device__ __forceinline__ lane::Vals residual32(const ResidualArgs& a, int n, int c0) {
 #pragma clang fp contract(off)
-    const int hpr = K >> 5;   // 32-channel halves per row (even)
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= (int64_t)N * hpr) return;   // whole pairs: N * hpr is even
-    const int n = (int)(t / hpr), hg = (int)(t - (int64_t)n * hpr), c0 = 32 * hg;
+    const int K = a.K;
     double p[32];
 #pragma unroll
     for (int c = 0; c < 32; ++c) p[c] = 0.0;
-    for (int j = 0; j < r; ++j) {
-        const double u = (double)__uint_as_float((uint32_t)l2[(int64_t)n * r + j] << 16);
-        const uint4* lr = reinterpret_cast<const uint4*>(l1 + (int64_t)j * K + c0);
+    for (int j = 0; j < a.r; ++j) {
+        const double u = (double)__uint_as_float((uint32_t)a.l2[(int64_t)n * a.r + j] << 16);
+        const uint4* lr = reinterpret_cast<const uint4*>(a.l1 + (int64_t)j * K + c0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint4 v = lr[q];
@@ -116,9 +117,9 @@ __global__ __launch_bounds__(256) void residual_int4_kernel(const float* __restr
             }
         }
     }
-    lane::Vals v, keep;
-    const float4* wr = reinterpret_cast<const float4*>(w + (int64_t)n * K + c0);
-    const float4* sr = reinterpret_cast<const float4*>(smooth_inv + c0);
+    lane::Vals keep;
+    const float4* wr = reinterpret_cast<const float4*>(a.w + (int64_t)n * K + c0);
+    const float4* sr = reinterpret_cast<const float4*>(a.smooth_inv + c0);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const float4 wv = wr[q], sv = sr[q];
@@ -128,15 +129,25 @@ __global__ __launch_bounds__(256) void residual_int4_kernel(const float* __restr
             const int c = 4 * q + i;
             const double lam = 1.0 / (double)sf[i];
             const double wh = (double)wf[i] * lam;
-            const float rv = r > 0 ? (float)(wh - p[c] * lam) : (float)wh;
+            const float rv = a.r > 0 ? (float)(wh - p[c] * lam) : (float)wh;
             if (c & 1) keep.od[c >> 1] = rv;
             else keep.ev[c >> 1] = rv;
         }
     }
-    v = keep;
-    float a = lane::absmax32(v);
-    a = fmaxf(a, __shfl_xor(a, 1, 64));   // the group's other half
-    const float s = a / 7.0f;
+    return keep;
+}
+
+// INT4: per 64-channel group, the activation rule (s = absmax / 7, q = rne(R / s)).
+__global__ __launch_bounds__(256) void residual_int4_kernel(ResidualArgs a) {
+    const int hpr = a.K >> 5;   // 32-channel halves per row (even)
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)a.N * hpr) return;   // whole pairs: N * hpr is even
+    const int n = (int)(t / hpr), hg = (int)(t - (int64_t)n * hpr);
+    const lane::Vals keep = residual32(a, n, 32 * hg);
+    lane::Vals v = keep;
+    float am = lane::absmax32(v);
+    am = fmaxf(am, __shfl_xor(am, 1, 64));   // the group's other half
+    const float s = am / 7.0f;
     lane::int4_codes32_exact(v, s, [&] { v = keep; });
     uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -144,8 +155,43 @@ __global__ __launch_bounds__(256) void residual_int4_kernel(const float* __restr
         const uint32_t pair = ((uint32_t)(int)v.ev[i] & 15u) | (((uint32_t)(int)v.od[i] & 15u) << 4);
         d[i >> 2] |= pair << (8 * (i & 3));
     }
-    *reinterpret_cast<uint4*>(codes + (int64_t)n * (K / 2) + 16 * hg) = make_uint4(d[0], d[1], d[2], d[3]);
-    if ((hg & 1) == 0) scales[(int64_t)n * (K / 64) + (hg >> 1)] = s;
+    *reinterpret_cast<uint4*>(a.codes + (int64_t)n * (a.K / 2) + 16 * hg) = make_uint4(d[0], d[1], d[2], d[3]);
+    if ((hg & 1) == 0) reinterpret_cast<float*>(a.scales)[(int64_t)n * (a.K / 64) + (hg >> 1)] = s;
+}
+
+// NVFP4, first pass: max |R| over the layer (every lane takes part in the wave's reduction;
+// lanes past the end contribute 0), one atomic per wave.
+__global__ __launch_bounds__(256) void residual_absmax_kernel(ResidualArgs a) {
+    const int hpr = a.K >> 5;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    float am = 0.0f;
+    if (t < (int64_t)a.N * hpr) {
+        const int n = (int)(t / hpr), hg = (int)(t - (int64_t)n * hpr);
+        am = lane::absmax32(residual32(a, n, 32 * hg));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+    if ((threadIdx.x & 63) == 0) atomicMax(a.gmax, __float_as_uint(am));
+}
+
+// NVFP4, second pass: per-tensor S_w = fp32(max |R| / 2688) (2688 = 448 * 6, the largest
+// E4M3 scale times the largest E2M1 value), then the activation rule per 16-block.
+__global__ __launch_bounds__(256) void residual_nvfp4_kernel(ResidualArgs a) {
+    const int hpr = a.K >> 5;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)a.N * hpr) return;
+    const int n = (int)(t / hpr), hg = (int)(t - (int64_t)n * hpr);
+    const float S = __uint_as_float(*a.gmax) / 2688.0f;
+    const lane::Vals v = residual32(a, n, 32 * hg);
+    uint32_t d[4], sbs;
+    lane::nvfp4_codes32(v, S, d, sbs);
+    *reinterpret_cast<uint4*>(a.codes + (int64_t)n * (a.K / 2) + 16 * hg) = make_uint4(d[0], d[1], d[2], d[3]);
+    *reinterpret_cast<uint16_t*>((uint8_t*)a.scales + (int64_t)n * (a.K / 16) + 2 * hg) = (uint16_t)sbs;
+}
+
+__global__ void global_scale_kernel(unsigned* g) {
+    const float S = __uint_as_float(*g) / 2688.0f;
+    *reinterpret_cast<float*>(g) = S;
 }
 
 dim3 col_grid(int64_t rows, int K, int per_thread) {
@@ -170,13 +216,21 @@ void launch_smoothing_factors(int N, int K, const float* w, const float* x_absma
                        x_absmax, (const float*)w_absmax, K, smooth_inv);
 }
 
-void launch_quantize_residual(int N, int K, int r, const float* w, const float* smooth_inv,
-                              const void* l1, const void* l2, void* codes, float* scales,
-                              hipStream_t st) {
+void launch_quantize_residual(int N, int K, int r, bool nvfp4, const float* w,
+                              const float* smooth_inv, const void* l1, const void* l2, void* codes,
+                              void* scales, float* global_scale, hipStream_t st) {
+    const ResidualArgs a{w, smooth_inv, (const uint16_t*)l1, (const uint16_t*)l2, N, K, r,
+                         (uint8_t*)codes, scales, reinterpret_cast<unsigned*>(global_scale)};
     const int64_t threads = (int64_t)N * (K / 32);
-    hipLaunchKernelGGL(residual_int4_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, w,
-                       smooth_inv, (const uint16_t*)l1, (const uint16_t*)l2, N, K, r, (uint8_t*)codes,
-                       scales);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (!nvfp4) {
+        hipLaunchKernelGGL(residual_int4_kernel, grid, dim3(256), 0, st, a);
+        return;
+    }
+    hipLaunchKernelGGL(fill_zero_u32_kernel, dim3(1), dim3(256), 0, st, a.gmax, 1);
+    hipLaunchKernelGGL(residual_absmax_kernel, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(residual_nvfp4_kernel, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(global_scale_kernel, dim3(1), dim3(1), 0, st, a.gmax);
 }
 
 }  // namespace svdq

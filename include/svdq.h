@@ -246,13 +246,16 @@ svdq_status svdq_gemm_w4a4_packed_quantize_next(
  *   factor lambda = sqrt(x_absmax[k] / cw[k]) in binary64, 1 where it is not a positive
  *   finite number or either maximum is 0; writes smooth_inv[k] = fp32(1 / lambda), the
  *   activation kernel's input.  Exact given the maxima (correctly rounded binary64 steps).
- * svdq_quantize_residual (INT4): with lam = 1 / smooth_inv (binary64), the 4-bit residual
+ * svdq_quantize_residual: with lam = 1 / smooth_inv (binary64), the 4-bit residual
  *   R = fp32(w lam - (l2 l1) lam) of the smoothed weight once the low-rank branch (l1 bf16
  *   [rank, K] with smooth_inv absorbed, l2 bf16 [N, rank], the same factors the GEMM and
- *   the activation kernel take; may be NULL at rank 0) is taken out, quantized per
- *   64-channel group like the activations: wgt_codes [N, K/2] nibbles and wgt_scales
- *   [N, K/64] fp32, svdq_prepack_weight's inputs.  The low-rank product sums bf16 products
- *   in binary64, exact while each element's products span less than 2^37, so the codes and
+ *   the activation kernel take; may be NULL at rank 0) is taken out, quantized like the
+ *   activations.  INT4: wgt_codes [N, K/2] nibbles and wgt_scales [N, K/64] fp32,
+ *   svdq_prepack_weight's inputs; wgt_global_scale is unused (may be NULL).  NVFP4: the
+ *   per-tensor scale S_w = fp32(max |R| / 2688) is written to wgt_global_scale (one fp32
+ *   in device memory, the GEMM's weight_global_scale), then wgt_codes [N, K/2] E2M1 and
+ *   wgt_scales [N, K/16] E4M3 bytes under it.  The low-rank product sums bf16 products in
+ *   binary64, exact while each element's products span less than 2^37, so the codes and
  *   scales are those of the definition bit for bit.
  * The top-r factorization between the two (the branch's l1, l2 from the smoothed weight's
  * leading singular triplets) is a dense SVD left to the caller's linear-algebra library.
@@ -262,8 +265,8 @@ svdq_status svdq_calib_absmax(int64_t M, int32_t K, const void* x, float* absmax
 svdq_status svdq_smoothing_factors(const svdq_layer_cfg* cfg, const float* w, const float* x_absmax,
                                    float* w_absmax, float* smooth_inv, svdq_stream_t stream);
 svdq_status svdq_quantize_residual(const svdq_layer_cfg* cfg, const float* w, const float* smooth_inv,
-                                   const void* l1, const void* l2, void* wgt_codes, float* wgt_scales,
-                                   svdq_stream_t stream);
+                                   const void* l1, const void* l2, void* wgt_codes, void* wgt_scales,
+                                   float* wgt_global_scale, svdq_stream_t stream);
 
 /* LoRA adapters through the low-rank branch (page "Diffusers integra Nunchaku ...",
  * "Nunchaku Lite: integración y modelo de ejecución": LoRA keeps working because the module

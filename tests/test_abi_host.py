@@ -182,12 +182,13 @@ def test_weight_quantizer_argument_rules():
     cfg = bd.LayerCfg.make(256, 128, 16)
     assert L.svdq_smoothing_factors(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
     assert "w_absmax" in bd.svdq_last_error()
-    assert L.svdq_quantize_residual(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, FAKE,
+    assert L.svdq_quantize_residual(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
                                     None) == bd.SVDQ_ERR_INVALID_ARG
     assert "l1" in bd.svdq_last_error()
     nv = bd.LayerCfg.make(256, 128, 16, "nvfp4")
-    assert L.svdq_quantize_residual(ctypes.byref(nv), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                    None) == bd.SVDQ_ERR_UNSUPPORTED_CONFIG
+    assert L.svdq_quantize_residual(ctypes.byref(nv), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                    None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "wgt_global_scale" in bd.svdq_last_error()
 
 
 def test_python_binding_raises_with_message():

@@ -1,7 +1,8 @@
 """GPU parity of the offline weight quantizer against the oracle's construction, bit for
 bit: the calibration absmax (accumulated over two batches), the smoothing factors (including
 channels whose activation or weight maximum is zero), and the INT4 residual's codes and
-scales given the oracle's top-r factors, at ranks 0 to 64 and on a 3072-channel layer."""
+scales given the oracle's top-r factors, INT4 and NVFP4 (with its per-tensor scale), at
+ranks 0 to 64 and on a 3072-channel layer."""
 import numpy as np
 import pytest
 import torch
@@ -74,4 +75,31 @@ def test_quantize_residual(N, K, r):
                               gu.dev(l2) if r else None, codes, scales)
     gc, gs = gu.host(codes), gu.host(scales)
     assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
+    assert np.array_equal(gc, oc), f"codes differ in {np.count_nonzero(gc != oc)} bytes"
+
+
+@pytest.mark.parametrize("N,K,r", [(200, 320, 16), (96, 128, 0), (1024, 3072, 32)])
+def test_quantize_residual_nvfp4(N, K, r):
+    """NVFP4: S_w = fp32(max |R32| / 2688), then E4M3 block scales and E2M1 codes, against
+    the oracle's construction bit for bit."""
+    rng = np.random.default_rng(1640 + N + K + r)
+    print(f"residual nvfp4 N={N} K={K} r={r}", flush=True)
+    x = synth.random_bf16(rng, (128, K), 1.0)
+    w = rng.normal(0.0, 0.02, (N, K)).astype(np.float32)
+    w[3, 17] = 0.9                                     # one large weight sets S_w
+    w64 = w.astype(np.float64)
+    si, lam = smoothing(x, w64)
+    l1, l2, R, _ = lowrank_residual(w64, si, lam, r)
+    R32 = R.astype(np.float32)
+    Sw = np.float32(np.max(np.abs(R32)) / np.float32(2688.0))
+    oc, os_ = oracle.quant_rows_nvfp4(R32, Sw)
+    cfg = bd.LayerCfg.make(K, N, r, "nvfp4")
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda:0")
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device="cuda:0")
+    gs = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    bd.svdq_quantize_residual(cfg, gu.dev(w), gu.dev(si), gu.dev(l1) if r else None,
+                              gu.dev(l2) if r else None, codes, scales, gs)
+    assert gu.host(gs).view(np.uint32)[0] == np.array([Sw], np.float32).view(np.uint32)[0]
+    assert np.array_equal(gu.host(scales), os_), "block scales differ"
+    gc = gu.host(codes)
     assert np.array_equal(gc, oc), f"codes differ in {np.count_nonzero(gc != oc)} bytes"
