@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times:
   attention projection 4096x3072x3072 r32 (INT4), the DiT MLP pair 4608x3072->12288->3072
-  with GELU (INT4), the fused-QKV NVFP4 projection 4096x3072x9216 r32 and the AWQ GEMV
-  2x3072x18432.  Weights come from the oracle's offline construction (smoothing factors,
-  top-r factors, quantized residual).
+  with GELU (INT4), the fused-QKV NVFP4 projection 4096x3072x9216 r32, the AWQ GEMV
+  2x3072x18432, the MLP with fc2's activation kernel fused into fc1's epilogue, and the
+  offline weight quantizer.  Weights come from the oracle's offline construction
+  (smoothing factors, top-r factors, quantized residual).
 
 Per stage, the GPU kernel is fed the oracle's inputs (never the other way round): the
 activation kernel is compared in full (codes and scales bit-exact, lora_act within its
@@ -229,3 +230,57 @@ def test_mlp_pair_packed(workload_cache):
     e2e = gu.rel_fro(y[rows], y2)
     print(f"mlp packed end-to-end rel_fro={e2e:.3e}")
     assert e2e <= 1e-3
+
+
+def test_mlp_fused_epilogue_fullsize(workload_cache):
+    """The MLP pair with fc2's activation kernel fused into fc1's epilogue, at the full size
+    and in the launch configuration the benchmark times: fc2's packed codes, scale words and
+    fp32 scales bit-identical to fc1 (bf16 out) followed by fc2's activation kernel, and
+    fc2's lora_act on sampled rows within the fp32 bound of the oracle's down-projection of
+    the same bf16 intermediate."""
+    d, (L1, L2) = _get(workload_cache, 2)
+    M, K1 = d.x_bf16.shape
+    N1 = L1["wcodes"].shape[0]
+    b1, _, gl1 = gu.quantize_packed(d.x_bf16, L1["smooth_inv"], L1["l1"])
+    wp1 = gu.prepack(L1["wcodes"], L1["wscales"], K1, N1)
+    h = gu.gemm_packed(b1, wp1, M, K1, N1, gl1, L1["l2"], L1["bias"], act=1, out_bf16=True)
+    ub, us, _ = gu.quantize_packed(h, L2["smooth_inv"], L2["l1"])
+    fb, fs, fl = gu.gemm_packed_quantize_next(b1, wp1, M, K1, N1, gl1, L1["l2"], L1["bias"], 1,
+                                              L2["smooth_inv"], L2["l1"])
+    torch.cuda.synchronize()
+    assert torch.equal(fb, ub), f"packed bytes differ in {int((fb != ub).sum())} places"
+    assert torch.equal(fs.view(torch.int32), us.view(torch.int32)), "fp32 scales differ"
+    rng = np.random.default_rng(22)
+    rows = np.unique(np.concatenate([rng.integers(0, M, 60), [0, M - 1]]))
+    hb = gu.host(h)[rows]
+    ol = oracle.quant_act_int4(hb, L2["smooth_inv"], L2["l1"])[2]
+    gu.assert_lora_close(gu.host(fl)[rows], ol, hb, L2["l1"])
+
+
+def test_weight_quantizer_fullsize(workload_cache):
+    """The offline weight quantizer on the attention projection's weight (3072 x 3072, rank
+    32, 4096 calibration tokens), bit-exact against the oracle's construction from the same
+    fp32 weight: calibration absmax, smoothing factors, INT4 residual codes and scales."""
+    import bit_diffusion_amd as bd
+    from oracle.construct import lowrank_residual, smoothing
+    d, (L,) = _get(workload_cache, 1)
+    w32 = np.ascontiguousarray(d.w.astype(np.float32))
+    N, K = w32.shape
+    r = L["rank"]
+    cfg = bd.LayerCfg.make(K, N, r)
+    am = torch.zeros(K, dtype=torch.float32, device="cuda:0")
+    bd.svdq_calib_absmax(d.x_bf16.shape[0], K, gu.dev(d.x_bf16), am)
+    wam = torch.empty(K, dtype=torch.float32, device="cuda:0")
+    si = torch.empty(K, dtype=torch.float32, device="cuda:0")
+    wd = gu.dev(w32)
+    bd.svdq_smoothing_factors(cfg, wd, am, wam, si)
+    osi, lam = smoothing(d.x_bf16, w32.astype(np.float64))
+    assert np.array_equal(gu.host(si).view(np.uint32), osi.view(np.uint32))
+    l1, l2, R, _ = lowrank_residual(w32.astype(np.float64), osi, lam, r)
+    oc, os_ = oracle.quant_rows_int4(R.astype(np.float32))
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda:0")
+    scales = torch.empty((N, K // 64), dtype=torch.float32, device="cuda:0")
+    bd.svdq_quantize_residual(cfg, wd, si, gu.dev(l1), gu.dev(l2), codes, scales)
+    assert np.array_equal(gu.host(scales).view(np.uint32), os_.view(np.uint32)), "scales differ"
+    gc = gu.host(codes)
+    assert np.array_equal(gc, oc), f"codes differ in {np.count_nonzero(gc != oc)} bytes"

@@ -67,3 +67,55 @@ def test_packed_linear_graph_replays(M, K, N, out_dtype, exact):
         torch.cuda.synchronize()
         if exact:
             assert torch.equal(out, eager)
+
+
+def test_fused_mlp_graph_replays():
+    """The MLP with fc2's activation kernel in fc1's epilogue (the workspace zeroing is a
+    fill kernel, the partial low-rank sums fp32 atomics) captured in a graph: every replay's
+    packed codes and scales bit-identical to the eager launch's, fc2's lora_act within one
+    bf16 ulp, with eager work between the replays."""
+    M, K1, N1, r = 700, 512, 768, 32
+    rng = np.random.default_rng(960)
+    dev = "cuda:0"
+    x = gu.dev(synth.random_bf16(rng, (M, K1), 1.0))
+    si1 = gu.dev(rng.uniform(0.5, 2.0, K1).astype(np.float32))
+    wpk = gu.prepack(synth.random_packed_nibbles(rng, N1, K1),
+                     rng.uniform(0.001, 0.05, (N1, K1 // 64)).astype(np.float32), K1, N1)
+    l1p = gu.prepack_l1(synth.random_bf16(rng, (r, K1), 0.05), K1)
+    l2 = gu.dev(synth.random_bf16(rng, (N1, r), 0.1))
+    b = gu.dev(synth.random_bf16(rng, (N1,), 0.3))
+    si2 = gu.dev(rng.uniform(0.5, 2.0, N1).astype(np.float32))
+    nl1 = gu.dev(synth.random_bf16(rng, (r, N1), 0.05))
+    cfg, ncfg = bd.LayerCfg.make(K1, N1, r), bd.LayerCfg.make(N1, 1, r)
+    apk = torch.empty(bd.svdq_act_packed_bytes(cfg, M), dtype=torch.uint8, device=dev)
+    lora = torch.empty((M, r), dtype=torch.int16, device=dev)
+    npk = torch.empty(bd.svdq_act_packed_bytes(ncfg, M), dtype=torch.uint8, device=dev)
+    nsc = torch.empty((M, N1 // 64), dtype=torch.float32, device=dev)
+    nlora = torch.empty((M, r), dtype=torch.int16, device=dev)
+    work = torch.empty((M, r), dtype=torch.float32, device=dev)
+
+    def step(stream):
+        sp = stream.cuda_stream
+        bd.svdq_quantize_act_packed(cfg, M, x, si1, l1p, apk, None, lora, sp)
+        bd.svdq_gemm_w4a4_packed_quantize_next(cfg, M, apk, wpk, lora, l2, b, bd.SVDQ_ACT_GELU_TANH,
+                                               ncfg, si2, nl1, npk, nsc, nlora, work, sp)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    e_pk, e_sc, e_lo = npk.clone(), nsc.clone(), gu.host(nlora)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step(side)
+    torch.cuda.synchronize()
+    for k in range(3):
+        npk.zero_()                        # eager work between replays
+        nlora.zero_()
+        work.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(npk, e_pk), f"replay {k}: packed codes differ"
+        assert torch.equal(nsc.view(torch.int32), e_sc.view(torch.int32)), f"replay {k}: scales differ"
+        assert gu.bf16_ulp_diff(gu.host(nlora), e_lo).max() <= 1, f"replay {k}: lora_act differs"
