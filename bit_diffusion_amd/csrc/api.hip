@@ -429,7 +429,7 @@ svdq_status svdq_calib_absmax(int64_t M, int32_t K, const void* x, float* absmax
         return fail(SVDQ_ERR_INVALID_ARG, "K = %d must be a positive multiple of 64", K);
     if (M > 0) SVDQ_TRY(check_ptr(x, "x", 16));
     SVDQ_TRY(check_ptr(absmax, "absmax", 16));
-    if ((M + 31) / 32 >= 65536)
+    if ((M + 63) / 64 >= 65536)
         return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
     SVDQ_TRY(check_current_device());
     if (M == 0) return SVDQ_OK;

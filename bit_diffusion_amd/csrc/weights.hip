@@ -13,29 +13,46 @@ namespace svdq {
 namespace {
 
 constexpr int kColThreads = 256, kColRows = 32;   // column pieces per block, rows per block
+constexpr int kCalPieces = 64, kCalGroups = 4, kCalRows = 16;   // calibration block shape
 
-// out[c] = max(out[c], max over this block's rows of |x[r, c]|) for bf16 x [M, K], 8 columns
-// per thread.  |x| as fp32 bits: non-negative floats order like their bit patterns (a NaN
-// ranks above every number, so it survives the max as it does in the definition's max).
-__global__ __launch_bounds__(kColThreads) void col_absmax_bf16_kernel(const uint16_t* __restrict__ x,
-                                                                      int64_t M, int K,
-                                                                      unsigned* __restrict__ out) {
-    const int c8 = blockIdx.x * kColThreads + threadIdx.x;
-    if (8 * c8 >= K) return;
-    const int64_t r0 = (int64_t)blockIdx.y * kColRows, r1 = min(M, r0 + kColRows);
+// out[c] = max(out[c], max |x[r, c]|) over bf16 x [M, K].  A block covers 64 pieces of 8
+// columns and 64 rows: its four waves take 16 rows each (16 loads in flight per lane), the
+// LDS combines the four, and one atomic per column leaves the block.  |x| as fp32 bits:
+// non-negative floats order like their bit patterns (a NaN ranks above every number, so it
+// survives the max as it does in the definition's max).
+__global__ __launch_bounds__(kCalPieces * kCalGroups) void col_absmax_bf16_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int K, unsigned* __restrict__ out) {
+    __shared__ uint32_t part[kCalGroups][8][kCalPieces];
+    const int pc = threadIdx.x & (kCalPieces - 1), grp = threadIdx.x / kCalPieces;
+    const int c8 = blockIdx.x * kCalPieces + pc;
+    const bool ok = 8 * c8 < K;
+    const int64_t r0 = (int64_t)blockIdx.y * (kCalRows * kCalGroups) + grp * kCalRows;
     uint32_t m[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll 8
-    for (int64_t r = r0; r < r1; ++r) {
-        const uint4 v = *reinterpret_cast<const uint4*>(x + r * K + 8 * c8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m[2 * i] = max(m[2 * i], (w[i] & 0x7FFFu) << 16);
-            m[2 * i + 1] = max(m[2 * i + 1], w[i] & 0x7FFF0000u);
+    for (int i = 0; i < kCalRows; ++i) {
+        const int64_t r = r0 + i;
+        if (ok && r < M) {
+            const uint4 v = *reinterpret_cast<const uint4*>(x + r * K + 8 * c8);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                m[2 * j] = max(m[2 * j], (w[j] & 0x7FFFu) << 16);
+                m[2 * j + 1] = max(m[2 * j + 1], w[j] & 0x7FFF0000u);
+            }
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) atomicMax(out + 8 * c8 + i, m[i]);
+    for (int j = 0; j < 8; ++j) part[grp][j][pc] = m[j];
+    __syncthreads();
+    if (grp == 0 && ok) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t v = part[0][j][pc];
+#pragma unroll
+            for (int q = 1; q < kCalGroups; ++q) v = max(v, part[q][j][pc]);
+            atomicMax(out + 8 * c8 + j, v);
+        }
+    }
 }
 
 // the same over fp32 w [N, K], 4 columns per thread
@@ -202,7 +219,9 @@ dim3 col_grid(int64_t rows, int K, int per_thread) {
 }  // namespace
 
 void launch_calib_absmax(int64_t M, int K, const void* x, float* absmax, hipStream_t st) {
-    hipLaunchKernelGGL(col_absmax_bf16_kernel, col_grid(M, K, 8), dim3(kColThreads), 0, st,
+    const dim3 grid((unsigned)((K / 8 + kCalPieces - 1) / kCalPieces),
+                    (unsigned)((M + kCalRows * kCalGroups - 1) / (kCalRows * kCalGroups)));
+    hipLaunchKernelGGL(col_absmax_bf16_kernel, grid, dim3(kCalPieces * kCalGroups), 0, st,
                        (const uint16_t*)x, M, K, reinterpret_cast<unsigned*>(absmax));
 }
 
