@@ -296,8 +296,9 @@ def mlp_leg(steps, sp, stream):
 
 def weights_leg(steps, sp, stream):
     """Offline weight quantization of the attention projection (N = K = 3072, rank 32):
-    calibration absmax over 4096 bf16 tokens, smoothing factors from an fp32 weight, and the
-    INT4 residual given bf16 top-r factors (the factorization itself is the caller's SVD).
+    calibration absmax over 4096 bf16 tokens, smoothing factors from an fp32 weight, the
+    INT4 residual given bf16 top-r factors, and the top-r factorization (block 48, four
+    power iterations).
     Algorithmic bytes: calibration reads x; smoothing reads w; the residual reads w, l1,
     l2, smooth_inv and writes the codes and scales."""
     import torch
@@ -319,11 +320,18 @@ def weights_leg(steps, sp, stream):
     calib = lambda i: bd.svdq_calib_absmax(Mc, K, x, am, sp)
     smooth = lambda i: bd.svdq_smoothing_factors(cfg, w, am, wam, si, sp)
     resid = lambda i: bd.svdq_quantize_residual(cfg, w, si, l1, l2, codes, scales, None, sp)
-    for f in (calib, smooth, resid):
+    Bw, It = 48, 4
+    omega = torch.randn((K, Bw), device=dev, generator=g)
+    f1 = torch.empty((Rw, K), dtype=torch.int16, device=dev)
+    f2 = torch.empty((N, Rw), dtype=torch.int16, device=dev)
+    ws = torch.empty(bd.svdq_lowrank_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    factor = lambda i: bd.svdq_lowrank_factors(cfg, w, si, omega, Bw, It, f1, f2, None, ws, sp)
+    for f in (calib, smooth, resid, factor):
         f(0)
     torch.cuda.synchronize()
     n = max(5, steps // 5)
     ms_c, ms_s, ms_r = (time_launches(f, n, stream) for f in (calib, smooth, resid))
+    ms_f = time_launches(factor, 3, stream)
     b_c = Mc * K * 2 + K * 4
     b_s = N * K * 4 + 3 * K * 4
     b_r = N * K * 4 + Rw * K * 2 + N * Rw * 2 + K * 4 + N * K // 2 + N * (K // 64) * 4
@@ -332,7 +340,8 @@ def weights_leg(steps, sp, stream):
             "calib_absmax_ms": round(ms_c, 4), "calib_absmax_GBs": round(b_c / (ms_c * 1e-3) / 1e9, 1),
             "smoothing_factors_ms": round(ms_s, 4), "smoothing_factors_GBs": round(b_s / (ms_s * 1e-3) / 1e9, 1),
             "quantize_residual_ms": round(ms_r, 4), "quantize_residual_GBs": round(b_r / (ms_r * 1e-3) / 1e9, 1),
-            "quantize_residual_fp64_TFLOPs": round(fp64 / (ms_r * 1e-3) / 1e12, 2)}
+            "quantize_residual_fp64_TFLOPs": round(fp64 / (ms_r * 1e-3) / 1e12, 2),
+            "lowrank_factors_ms": round(ms_f, 3), "lowrank_block": Bw, "lowrank_iters": It}
 
 
 def lora_leg(steps, sp, stream, si, sets):

@@ -21,7 +21,7 @@ __all__ = [
     "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
     "svdq_prepacked_l1_bytes", "svdq_prepack_l1", "svdq_merged_rank", "svdq_merge_lora",
     "svdq_gemm_w4a4_packed_quantize_next", "svdq_calib_absmax", "svdq_smoothing_factors",
-    "svdq_quantize_residual",
+    "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -158,6 +158,19 @@ def svdq_quantize_residual(cfg, w, smooth_inv, l1, l2, wgt_codes, wgt_scales, wg
     return _check(lib().svdq_quantize_residual(ctypes.byref(cfg), _ptr(w), _ptr(smooth_inv),
                                                _ptr(l1), _ptr(l2), _ptr(wgt_codes), _ptr(wgt_scales),
                                                _ptr(wgt_global_scale), _stream(stream)))
+
+
+def svdq_lowrank_workspace_bytes(cfg):
+    n = ctypes.c_int64(0)
+    _check(lib().svdq_lowrank_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def svdq_lowrank_factors(cfg, w, smooth_inv, omega, block, iters, l1, l2, sigma, workspace,
+                         stream=None):
+    return _check(lib().svdq_lowrank_factors(ctypes.byref(cfg), _ptr(w), _ptr(smooth_inv),
+                                             _ptr(omega), int(block), int(iters), _ptr(l1), _ptr(l2),
+                                             _ptr(sigma), _ptr(workspace), _stream(stream)))
 
 
 def svdq_check_device(device=0):

@@ -28,7 +28,7 @@ EXPORTS = ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_
            "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
            "svdq_prepacked_l1_bytes", "svdq_prepack_l1", "svdq_merged_rank", "svdq_merge_lora",
            "svdq_gemm_w4a4_packed_quantize_next", "svdq_calib_absmax", "svdq_smoothing_factors",
-           "svdq_quantize_residual")
+           "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors")
 
 
 class LayerCfg(ctypes.Structure):
@@ -82,6 +82,8 @@ def lib():
         L.svdq_calib_absmax.argtypes = [I64, I32, P, P, P]
         L.svdq_smoothing_factors.argtypes = [cfgp, P, P, P, P, P]
         L.svdq_quantize_residual.argtypes = [cfgp, P, P, P, P, P, P, P, P]
+        L.svdq_lowrank_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_int64)]
+        L.svdq_lowrank_factors.argtypes = [cfgp, P, P, P, I32, I32, P, P, P, P, P]
         L.svdq_gemm_w4a4_packed.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P]
         L.svdq_check_device.argtypes = [ctypes.c_int]
         L.svdq_check_arch.argtypes = [ctypes.c_char_p]
@@ -95,7 +97,8 @@ def lib():
                      "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed", "svdq_pack_act",
                      "svdq_prepack_weight", "svdq_gemm_w4a4_packed", "svdq_prepacked_l1_bytes",
                      "svdq_prepack_l1", "svdq_merge_lora", "svdq_gemm_w4a4_packed_quantize_next",
-                     "svdq_calib_absmax", "svdq_smoothing_factors", "svdq_quantize_residual"):
+                     "svdq_calib_absmax", "svdq_smoothing_factors", "svdq_quantize_residual",
+                     "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -475,6 +475,36 @@ svdq_status svdq_quantize_residual(const svdq_layer_cfg* cfg, const float* w, co
     return after_launch("svdq_quantize_residual");
 }
 
+svdq_status svdq_lowrank_workspace_bytes(const svdq_layer_cfg* cfg, int64_t* bytes) {
+    SVDQ_TRY(check_cfg(cfg));
+    if (bytes == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = svdq::lowrank_workspace_bytes(cfg->out_features, cfg->in_features);
+    return SVDQ_OK;
+}
+
+svdq_status svdq_lowrank_factors(const svdq_layer_cfg* cfg, const float* w, const float* smooth_inv,
+                                 const float* omega, int32_t block, int32_t iters, void* l1, void* l2,
+                                 float* sigma, void* workspace, svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    const int r = cfg->rank;
+    if (r <= 0 || r > 64)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "rank %d: the factorization takes ranks 16 to 64", r);
+    if (block < r || block > 64)
+        return fail(SVDQ_ERR_INVALID_ARG, "block %d must lie in [rank %d, 64]", block, r);
+    if (iters < 0 || iters > 32) return fail(SVDQ_ERR_INVALID_ARG, "iters %d must lie in [0, 32]", iters);
+    SVDQ_TRY(check_ptr(w, "w", 4));
+    SVDQ_TRY(check_ptr(smooth_inv, "smooth_inv", 4));
+    SVDQ_TRY(check_ptr(omega, "omega", 4));
+    SVDQ_TRY(check_ptr(l1, "l1", 2));
+    SVDQ_TRY(check_ptr(l2, "l2", 2));
+    if (sigma != nullptr && !aligned(sigma, 4)) return fail(SVDQ_ERR_INVALID_ARG, "sigma is not 4-byte aligned");
+    SVDQ_TRY(check_ptr(workspace, "workspace", 16));
+    SVDQ_TRY(check_current_device());
+    svdq::launch_lowrank_factors(cfg->out_features, cfg->in_features, r, block, iters, w, smooth_inv, omega,
+                                 l1, l2, sigma, workspace, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_lowrank_factors");
+}
+
 svdq_status svdq_check_device(int device) { return check_device_ordinal(device); }
 
 svdq_status svdq_check_arch(const char* arch_name) {

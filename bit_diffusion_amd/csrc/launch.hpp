@@ -98,4 +98,10 @@ void launch_quantize_residual(int N, int K, int r, bool nvfp4, const float* w,
                               const float* smooth_inv, const void* l1, const void* l2, void* codes,
                               void* scales, float* global_scale, hipStream_t st);
 
+// top-r factorization of the smoothed weight (lowrank.hip)
+int64_t lowrank_workspace_bytes(int N, int K);
+void launch_lowrank_factors(int N, int K, int r, int b, int iters, const float* w,
+                            const float* smooth_inv, const float* omega, void* l1, void* l2,
+                            float* sigma_out, void* workspace, hipStream_t st);
+
 }  // namespace svdq

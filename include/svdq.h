@@ -257,8 +257,16 @@ svdq_status svdq_gemm_w4a4_packed_quantize_next(
  *   wgt_scales [N, K/16] E4M3 bytes under it.  The low-rank product sums bf16 products in
  *   binary64, exact while each element's products span less than 2^37, so the codes and
  *   scales are those of the definition bit for bit.
- * The top-r factorization between the two (the branch's l1, l2 from the smoothed weight's
- * leading singular triplets) is a dense SVD left to the caller's linear-algebra library.
+ * svdq_lowrank_factors: the branch's factors between the two, from the leading r singular
+ *   triplets of the smoothed weight W diag(lambda) (lambda = 1 / smooth_inv), split as
+ *   sqrt(sigma) on each side: l2 bf16 [N, r] = U sqrt(sigma), l1 bf16 [r, K] =
+ *   sqrt(sigma) V^T diag(smooth_inv); sigma (fp32 [r], may be NULL) the singular values in
+ *   decreasing order.  Computed by randomized subspace iteration (Halko, Martinsson and
+ *   Tropp 2011): omega is the caller's fp32 [K, block] standard-normal draws, r <= block
+ *   <= 64 (oversampling block - r), `iters` power iterations (0 to 32); the result
+ *   approximates the exact triplets (exact for a weight of rank <= block), closer with more
+ *   oversampling and iterations.  rank 16 to 64.  workspace: device memory of
+ *   svdq_lowrank_workspace_bytes(cfg) bytes, 16-byte aligned, overwritten.
  * All buffers are device memory owned by the caller; all enqueue on `stream`. */
 svdq_status svdq_calib_absmax(int64_t M, int32_t K, const void* x, float* absmax,
                               svdq_stream_t stream);
@@ -267,6 +275,10 @@ svdq_status svdq_smoothing_factors(const svdq_layer_cfg* cfg, const float* w, co
 svdq_status svdq_quantize_residual(const svdq_layer_cfg* cfg, const float* w, const float* smooth_inv,
                                    const void* l1, const void* l2, void* wgt_codes, void* wgt_scales,
                                    float* wgt_global_scale, svdq_stream_t stream);
+svdq_status svdq_lowrank_workspace_bytes(const svdq_layer_cfg* cfg, int64_t* bytes);
+svdq_status svdq_lowrank_factors(const svdq_layer_cfg* cfg, const float* w, const float* smooth_inv,
+                                 const float* omega, int32_t block, int32_t iters, void* l1, void* l2,
+                                 float* sigma, void* workspace, svdq_stream_t stream);
 
 /* LoRA adapters through the low-rank branch (page "Diffusers integra Nunchaku ...",
  * "Nunchaku Lite: integración y modelo de ejecución": LoRA keeps working because the module

@@ -191,6 +191,20 @@ def test_weight_quantizer_argument_rules():
     assert "wgt_global_scale" in bd.svdq_last_error()
 
 
+def test_lowrank_factor_argument_rules():
+    L = bd.lib()
+    f = L.svdq_lowrank_factors
+    big = bd.LayerCfg.make(512, 256, 80)
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, 80, 2, FAKE, FAKE, None, FAKE, None) == bd.SVDQ_ERR_UNSUPPORTED_CONFIG
+    cfg = bd.LayerCfg.make(512, 256, 32)
+    assert f(ctypes.byref(cfg), FAKE, FAKE, FAKE, 16, 2, FAKE, FAKE, None, FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "block" in bd.svdq_last_error()
+    assert f(ctypes.byref(cfg), FAKE, FAKE, FAKE, 48, 99, FAKE, FAKE, None, FAKE, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(cfg), FAKE, FAKE, FAKE, 48, 2, FAKE, FAKE, None, None, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "workspace" in bd.svdq_last_error()
+    assert bd.svdq_lowrank_workspace_bytes(cfg) > 0
+
+
 def test_python_binding_raises_with_message():
     cfg = bd.LayerCfg.make(100, 512, 16)
     with pytest.raises(bd.SvdqError) as e:
