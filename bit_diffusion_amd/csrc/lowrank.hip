@@ -97,15 +97,21 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restri
     }
 }
 
-// Sum the partial Gram matrices into LDS (b x b used), one wave.
+// Sum the partial Gram matrices into LDS (b x b used), one wave: lane t keeps column t of
+// all 64 rows in registers, so each partial's 64 loads are independent.
 __device__ void sum_gram(const double* part, int nblk, int b, double (*G)[kW]) {
     const int t = threadIdx.x;
-    for (int i = 0; i < kW; ++i) {
-        double s = 0.0;
-        if (i < b && t < b)
-            for (int k = 0; k < nblk; ++k) s += part[(int64_t)k * kW * kW + i * kW + t];
-        G[i][t] = s;
-    }
+    double acc[kW];
+#pragma unroll
+    for (int i = 0; i < kW; ++i) acc[i] = 0.0;
+    if (t < b)
+        for (int k = 0; k < nblk; ++k) {
+            const double* pk = part + (int64_t)k * kW * kW + t;
+#pragma unroll
+            for (int i = 0; i < kW; ++i) acc[i] += pk[i * kW];
+        }
+#pragma unroll
+    for (int i = 0; i < kW; ++i) G[i][t] = i < b ? acc[i] : 0.0;
     __syncthreads();
 }
 
@@ -169,7 +175,6 @@ __global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ p
                                                     float* __restrict__ ub, float* __restrict__ sigma) {
     __shared__ double S[kW][kW];
     __shared__ double V[kW][kW];
-    __shared__ double rot[2];
     __shared__ int order[kW];
     const int t = threadIdx.x;
     sum_gram(part, nblk, b, S);
@@ -182,19 +187,16 @@ __global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ p
         if (off <= 1e-26 * dia) break;   // every lane sees the same S
         for (int p = 0; p < b - 1; ++p)
             for (int q = p + 1; q < b; ++q) {
-                if (t == 0) {
-                    const double apq = S[p][q];
-                    double c = 1.0, s = 0.0;
-                    if (fabs(apq) > 1e-300) {
-                        const double th = (S[q][q] - S[p][p]) / (2.0 * apq);
-                        const double tt = (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + __builtin_sqrt(th * th + 1.0));
-                        c = 1.0 / __builtin_sqrt(tt * tt + 1.0);
-                        s = tt * c;
-                    }
-                    rot[0] = c, rot[1] = s;
+                // every lane derives the same rotation from the same three entries
+                const double apq = S[p][q];
+                double c = 1.0, s = 0.0;
+                if (fabs(apq) > 1e-300) {
+                    const double th = (S[q][q] - S[p][p]) / (2.0 * apq);
+                    const double tt = (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + __builtin_sqrt(th * th + 1.0));
+                    c = 1.0 / __builtin_sqrt(tt * tt + 1.0);
+                    s = tt * c;
                 }
-                __syncthreads();
-                const double c = rot[0], s = rot[1];
+                __syncthreads();   // every lane has read S[p][q], S[p][p], S[q][q]
                 if (s != 0.0) {
                     if (t < b) {   // columns p, q
                         const double kp = S[t][p], kq = S[t][q];
