@@ -23,32 +23,37 @@ constexpr int kW = 64;   // stored width of every tall matrix, and the maximum b
 // Y[n, j] = sum_k W[n, k] lam_k X[k, j] (TRANS = false, rows = N, inner = K) or
 // Y[k, j] = lam_k sum_n W[n, k] X[n, j] (TRANS = true, rows = K, inner = N).
 // A block computes 64 rows x 64 columns; thread (ty, tx) rows 4 ty .. + 3, columns tx + 16 c.
+// The inner dimension is cut into gridDim.y slices of `chunk` (a multiple of 32); slice y
+// writes its partial product to Y + y * rows * 64 and sum_slices_kernel adds the slices in
+// a fixed order, so the result does not depend on scheduling.
 template <bool TRANS>
 __global__ __launch_bounds__(256) void skinny_kernel(const float* __restrict__ W,
                                                      const float* __restrict__ smooth_inv, int N,
-                                                     int K, const float* __restrict__ X,
+                                                     int K, const float* __restrict__ X, int chunk,
                                                      float* __restrict__ Y) {
     __shared__ float As[32][kW + 1];   // [inner][row]
     __shared__ float Bs[32][kW];       // [inner][column]
     const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
     const int rows = TRANS ? K : N, inner = TRANS ? N : K;
     const int r0 = blockIdx.x * kW;
+    const int ib = blockIdx.y * chunk, ie = min(inner, ib + chunk);
+    Y += (int64_t)blockIdx.y * rows * kW;
     float acc[4][4] = {};
-    for (int i0 = 0; i0 < inner; i0 += 32) {
+    for (int i0 = ib; i0 < ie; i0 += 32) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int idx = tid + 256 * e;   // 2048 elements of each tile
             if constexpr (!TRANS) {
                 const int rr = idx >> 5, ii = idx & 31;   // W[r0 + rr, i0 + ii] * lam
                 const int n = r0 + rr, k = i0 + ii;
-                As[ii][rr] = n < N && k < K ? W[(int64_t)n * K + k] / smooth_inv[k] : 0.0f;
+                As[ii][rr] = n < N && k < ie ? W[(int64_t)n * K + k] / smooth_inv[k] : 0.0f;
             } else {
                 const int ii = idx >> 6, rr = idx & 63;   // W[i0 + ii, r0 + rr]
                 const int n = i0 + ii, k = r0 + rr;
-                As[ii][rr] = n < N && k < K ? W[(int64_t)n * K + k] : 0.0f;
+                As[ii][rr] = n < ie && k < K ? W[(int64_t)n * K + k] : 0.0f;
             }
             const int bi = idx >> 6, bj = idx & 63;
-            Bs[bi][bj] = i0 + bi < inner ? X[(int64_t)(i0 + bi) * kW + bj] : 0.0f;
+            Bs[bi][bj] = i0 + bi < ie ? X[(int64_t)(i0 + bi) * kW + bj] : 0.0f;
         }
         __syncthreads();
 #pragma unroll 8
@@ -73,6 +78,16 @@ __global__ __launch_bounds__(256) void skinny_kernel(const float* __restrict__ W
 #pragma unroll
         for (int c = 0; c < 4; ++c) Y[(int64_t)r * kW + tx + 16 * c] = acc[q][c] * scale;
     }
+}
+
+// out[r, j] = sum over the slices s = 0, 1, ... of part[s][r, j], in that order
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part, int64_t n,
+                                                         int slices, float* __restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n) return;
+    float s = part[t];
+    for (int y = 1; y < slices; ++y) s += part[(int64_t)y * n + t];
+    out[t] = s;
 }
 
 // part[blk] = X[64 blk .. + 63, :]^T X[...] in binary64 (rows past `rows` are zero)
@@ -268,8 +283,10 @@ __global__ __launch_bounds__(256) void pad_kernel(const float* __restrict__ src,
     dst[t] = j < b ? src[r * b + j] : 0.0f;
 }
 
+constexpr int kSlices = 5;   // inner-dimension slices of a skinny product
+
 struct Work {
-    float *Q, *Z, *rinv, *ub, *sigma;
+    float *Q, *Z, *rinv, *ub, *sigma, *slices;
     double* part;
 };
 
@@ -279,6 +296,8 @@ Work carve(void* ws, int N, int K) {
     Work w;
     w.part = (double*)p;
     p += (int64_t)nblk * kW * kW * 8;
+    w.slices = (float*)p;
+    p += (int64_t)kSlices * std::max(N, K) * kW * 4;
     w.Q = (float*)p;
     p += (int64_t)N * kW * 4;
     w.Z = (float*)p;
@@ -289,6 +308,20 @@ Work carve(void* ws, int N, int K) {
     p += kW * kW * 4;
     w.sigma = (float*)p;
     return w;
+}
+
+// Y = W_hat X (TRANS false, Y [N, 64]) or W_hat^T X (TRANS true, Y [K, 64])
+template <bool TRANS>
+void skinny(const float* W, const float* smooth_inv, int N, int K, const float* X, float* Y,
+            const Work& w, hipStream_t st) {
+    const int rows = TRANS ? K : N, inner = TRANS ? N : K;
+    const int chunk = ((inner + kSlices - 1) / kSlices + 31) / 32 * 32;
+    const int slices = (inner + chunk - 1) / chunk;
+    hipLaunchKernelGGL(skinny_kernel<TRANS>, dim3((unsigned)((rows + kW - 1) / kW), (unsigned)slices), dim3(256),
+                       0, st, W, smooth_inv, N, K, X, chunk, w.slices);
+    const int64_t n = (int64_t)rows * kW;
+    hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float*)w.slices, n, slices, Y);
 }
 
 void orth(float* X, int rows, int b, const Work& w, hipStream_t st) {
@@ -305,25 +338,26 @@ void orth(float* X, int rows, int b, const Work& w, hipStream_t st) {
 
 int64_t lowrank_workspace_bytes(int N, int K) {
     const int nblk = (std::max(N, K) + kW - 1) / kW;
-    return (int64_t)nblk * kW * kW * 8 + (int64_t)(N + K) * kW * 4 + 2 * kW * kW * 4 + kW * 4;
+    return (int64_t)nblk * kW * kW * 8 + (int64_t)kSlices * std::max(N, K) * kW * 4 +
+           (int64_t)(N + K) * kW * 4 + 2 * kW * kW * 4 + kW * 4;
 }
 
 void launch_lowrank_factors(int N, int K, int r, int b, int iters, const float* w,
                             const float* smooth_inv, const float* omega, void* l1, void* l2,
                             float* sigma_out, void* workspace, hipStream_t st) {
     const Work wk = carve(workspace, N, K);
-    const dim3 gN((unsigned)((N + kW - 1) / kW)), gK((unsigned)((K + kW - 1) / kW));
+    const dim3 gK((unsigned)((K + kW - 1) / kW));
     hipLaunchKernelGGL(pad_kernel, dim3((unsigned)(((int64_t)K * kW + 255) / 256)), dim3(256), 0, st, omega, K,
                        b, wk.Z);
-    hipLaunchKernelGGL(skinny_kernel<false>, gN, dim3(256), 0, st, w, smooth_inv, N, K, (const float*)wk.Z, wk.Q);
+    skinny<false>(w, smooth_inv, N, K, wk.Z, wk.Q, wk, st);
     orth(wk.Q, N, b, wk, st);
     for (int it = 0; it < iters; ++it) {
-        hipLaunchKernelGGL(skinny_kernel<true>, gK, dim3(256), 0, st, w, smooth_inv, N, K, (const float*)wk.Q, wk.Z);
+        skinny<true>(w, smooth_inv, N, K, wk.Q, wk.Z, wk, st);
         orth(wk.Z, K, b, wk, st);
-        hipLaunchKernelGGL(skinny_kernel<false>, gN, dim3(256), 0, st, w, smooth_inv, N, K, (const float*)wk.Z, wk.Q);
+        skinny<false>(w, smooth_inv, N, K, wk.Z, wk.Q, wk, st);
         orth(wk.Q, N, b, wk, st);
     }
-    hipLaunchKernelGGL(skinny_kernel<true>, gK, dim3(256), 0, st, w, smooth_inv, N, K, (const float*)wk.Q, wk.Z);
+    skinny<true>(w, smooth_inv, N, K, wk.Q, wk.Z, wk, st);
     hipLaunchKernelGGL(gram_partial_kernel, gK, dim3(256), 0, st, (const float*)wk.Z, K, wk.part);
     hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(64), 0, st, (const double*)wk.part, (int)gK.x, b, wk.ub,
                        wk.sigma);
