@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restri
 
 // Sum the partial Gram matrices into LDS (b x b used), one wave: lane t keeps column t of
 // all 64 rows in registers, so each partial's 64 loads are independent.
-__device__ void sum_gram(const double* part, int nblk, int b, double (*G)[kW]) {
+__device__ void sum_gram(const double* part, int nblk, int b, double (*G)[kW + 1]) {
     const int t = threadIdx.x;
     double acc[kW];
 #pragma unroll
@@ -135,9 +135,9 @@ __device__ void sum_gram(const double* part, int nblk, int b, double (*G)[kW]) {
 // zeroes its column.  One wave of 64 lanes.
 __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ part, int nblk, int b,
                                                   float* __restrict__ rinv) {
-    __shared__ double G[kW][kW];
-    __shared__ double L[kW][kW];
-    __shared__ double Li[kW][kW];
+    __shared__ double G[kW][kW + 1];   // padded: column walks stay conflict-free
+    __shared__ double L[kW][kW + 1];   // padded: column walks stay conflict-free
+    __shared__ double Li[kW][kW + 1];   // padded: column walks stay conflict-free
     const int t = threadIdx.x;
     sum_gram(part, nblk, b, G);
     for (int i = 0; i < kW; ++i) L[i][t] = 0.0, Li[i][t] = 0.0;
@@ -188,48 +188,74 @@ __global__ __launch_bounds__(256) void apply_rinv_kernel(float* __restrict__ X, 
 // in decreasing order: ub[i][j] (64 x 64, the first r columns used), sigma[j] = sqrt(ev_j).
 __global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ part, int nblk, int b,
                                                     float* __restrict__ ub, float* __restrict__ sigma) {
-    __shared__ double S[kW][kW];
-    __shared__ double V[kW][kW];
+    __shared__ double S[kW][kW + 1];   // padded: column walks stay conflict-free
+    __shared__ double V[kW][kW + 1];   // padded: column walks stay conflict-free
     __shared__ int order[kW];
+    __shared__ int pp[kW / 2], pq[kW / 2];
+    __shared__ double pc[kW / 2], ps[kW / 2];
     const int t = threadIdx.x;
     sum_gram(part, nblk, b, S);
     for (int i = 0; i < kW; ++i) V[i][t] = i == t ? 1.0 : 0.0;
     __syncthreads();
+    // Parallel cyclic Jacobi, round-robin ordering: with nb = b rounded up to even, a sweep
+    // is nb - 1 rounds; round r pairs the positions i and nb - 1 - i of the list
+    // (0, 1 + (r mod (nb - 1)), ...), so every index pair meets once per sweep and the
+    // pairs of a round are disjoint.  Each round takes every pair's rotation from S as the
+    // round finds it, then applies all of them: columns (S and V), then rows.
+    const int nb = (b + 1) & ~1, np = nb / 2;
     for (int sweep = 0; sweep < 30; ++sweep) {
         double off = 0.0, dia = 0.0;
         for (int i = 0; i < b; ++i)
             for (int j = 0; j < b; ++j) (i == j ? dia : off) += S[i][j] * S[i][j];
-        if (off <= 1e-26 * dia) break;   // every lane sees the same S
-        for (int p = 0; p < b - 1; ++p)
-            for (int q = p + 1; q < b; ++q) {
-                // every lane derives the same rotation from the same three entries
-                const double apq = S[p][q];
-                double c = 1.0, s = 0.0;
-                if (fabs(apq) > 1e-300) {
-                    const double th = (S[q][q] - S[p][p]) / (2.0 * apq);
-                    const double tt = (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + __builtin_sqrt(th * th + 1.0));
-                    c = 1.0 / __builtin_sqrt(tt * tt + 1.0);
-                    s = tt * c;
-                }
-                __syncthreads();   // every lane has read S[p][q], S[p][p], S[q][q]
-                if (s != 0.0) {
-                    if (t < b) {   // columns p, q
-                        const double kp = S[t][p], kq = S[t][q];
-                        S[t][p] = c * kp - s * kq;
-                        S[t][q] = s * kp + c * kq;
-                        const double vp = V[t][p], vq = V[t][q];
-                        V[t][p] = c * vp - s * vq;
-                        V[t][q] = s * vp + c * vq;
-                    }
-                    __syncthreads();
-                    if (t < b) {   // rows p, q
-                        const double pk = S[p][t], qk = S[q][t];
-                        S[p][t] = c * pk - s * qk;
-                        S[q][t] = s * pk + c * qk;
+        if (off <= 1e-24 * dia) break;   // every lane sees the same S
+        for (int rd = 0; rd < nb - 1; ++rd) {
+            if (t < np) {
+                const int i0 = t, i1 = nb - 1 - t;
+                int p = i0 == 0 ? 0 : 1 + (i0 - 1 + rd) % (nb - 1);
+                int q = 1 + (i1 - 1 + rd) % (nb - 1);
+                if (p > q) { const int x = p; p = q; q = x; }
+                double c = 1.0, sn = 0.0;
+                if (q < b) {
+                    const double apq = S[p][q];
+                    if (fabs(apq) > 1e-300) {
+                        const double th = (S[q][q] - S[p][p]) / (2.0 * apq);
+                        // tan of the angle; 1 / (2 th) where th * th would overflow
+                        const double tt = fabs(th) > 1e150
+                                              ? 0.5 / th
+                                              : (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + __builtin_sqrt(th * th + 1.0));
+                        c = 1.0 / __builtin_sqrt(tt * tt + 1.0);
+                        sn = tt * c;
                     }
                 }
-                __syncthreads();
+                pp[t] = p, pq[t] = q, pc[t] = c, ps[t] = sn;
             }
+            __syncthreads();
+            for (int it = t; it < np * b; it += kW) {   // columns p, q of S and V
+                const int pr = it / b, k = it - pr * b;
+                const double sn = ps[pr];
+                if (sn == 0.0) continue;
+                const int p = pp[pr], q = pq[pr];
+                const double c = pc[pr];
+                const double kp = S[k][p], kq = S[k][q];
+                S[k][p] = c * kp - sn * kq;
+                S[k][q] = sn * kp + c * kq;
+                const double vp = V[k][p], vq = V[k][q];
+                V[k][p] = c * vp - sn * vq;
+                V[k][q] = sn * vp + c * vq;
+            }
+            __syncthreads();
+            for (int it = t; it < np * b; it += kW) {   // rows p, q of S
+                const int pr = it / b, k = it - pr * b;
+                const double sn = ps[pr];
+                if (sn == 0.0) continue;
+                const int p = pp[pr], q = pq[pr];
+                const double c = pc[pr];
+                const double pk = S[p][k], qk = S[q][k];
+                S[p][k] = c * pk - sn * qk;
+                S[q][k] = sn * pk + c * qk;
+            }
+            __syncthreads();
+        }
     }
     if (t == 0) {   // order by decreasing eigenvalue (selection)
         for (int i = 0; i < b; ++i) order[i] = i;
