@@ -57,8 +57,17 @@ def parse():
     ap.add_argument("--copies", type=int, default=10,
                     help="rotating input sets (each ~30 MB) to defeat the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1536,
+    ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the workload the CPU oracle baseline runs")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads of the CPU baseline (default: the cores this process "
+                         "may use, at most 16)")
+    ap.add_argument("--single-rows", type=int, default=256,
+                    help="token rows the CPU baseline also runs on one thread")
+    ap.add_argument("--reps", type=int, default=100,
+                    help="timed repetitions behind each median / p10 / p90")
+    ap.add_argument("--leg", choices=["awq", "nvfp4", "mlp", "weights", "peaks"], default=None,
+                    help="run one secondary leg alone and print its JSON (profiling runs)")
     ap.add_argument("--only-main", action="store_true",
                     help="time only the W4A4 linear (no AWQ / NVFP4 legs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -119,7 +128,38 @@ def time_launches(fn, n, stream):
     return e0.elapsed_time(e1) / n
 
 
-def awq_leg(steps, sp, stream):
+def launch_stats(fn, batch, reps):
+    """Per-call times (ms) of fn(i, stream_handle): `batch` calls captured once into a HIP
+    graph on a side stream, the graph replayed `reps` times with an event pair around each
+    replay on that stream (so each sample is the mean of `batch` back-to-back calls and the
+    events' own latency is spread over them).  Returns mean, median, p10, p90 (ms per call)
+    and the counts."""
+    import torch
+    cs = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(batch):
+                fn(i, cs.cuda_stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cs):
+        g.replay()                      # the first replay uploads the graph
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    with torch.cuda.stream(cs):
+        for a, b in ev:
+            a.record(cs)
+            g.replay()
+            b.record(cs)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) / batch for a, b in ev])
+    return {"mean": round(float(t.mean()), 5), "median": round(float(np.median(t)), 5),
+            "p10": round(float(np.percentile(t, 10)), 5),
+            "p90": round(float(np.percentile(t, 90)), 5), "reps": reps, "batch": batch}
+
+
+def awq_leg(reps, sp, stream):
     """AWQ W4A16 GEMV of the modulation layers: M=2, K=3072, N=18432, 14 rotating weight
     copies (> 400 MB, so every call streams its weights from HBM)."""
     import torch
@@ -140,21 +180,24 @@ def awq_leg(steps, sp, stream):
     b = t16(synth.random_bf16(rng, (Na,), 0.1))
     out = torch.empty((Ma, Na), dtype=torch.float32, device=dev)
 
-    def go(i):
+    def go(i, st=sp):
         k = i % copies
-        bd.awq_gemm_w4a16(Ma, Ka, Na, 64, x, qs[k], sc[k], zs[k], b, bd.SVDQ_DT_F32, out, sp)
+        bd.awq_gemm_w4a16(Ma, Ka, Na, 64, x, qs[k], sc[k], zs[k], b, bd.SVDQ_DT_F32, out, st)
 
     for i in range(copies):
         go(i)
     torch.cuda.synchronize()
-    ms = time_launches(go, max(steps, copies), stream)
+    st = launch_stats(go, 2 * copies, reps)
+    ms = st["mean"]
     nbytes = Na * Ka // 2 + 2 * Na * (Ka // 64) * 2 + Ma * Ka * 2 + Na * 2 + Ma * Na * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": "awq_modulation_2x3072x18432", "us_per_call": round(ms * 1e3, 3),
+            "us_median": round(st["median"] * 1e3, 3), "us_p10": round(st["p10"] * 1e3, 3),
+            "us_p90": round(st["p90"] * 1e3, 3), "reps": reps,
             "bytes": nbytes, "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def nvfp4_leg(steps, sp, stream):
+def nvfp4_leg(reps, sp, stream):
     """NVFP4 fused-QKV linear: activation kernel + GEMM, M=4096, K=3072, N=9216, rank 32."""
     import torch
     import synth
@@ -180,28 +223,41 @@ def nvfp4_leg(steps, sp, stream):
     out = torch.empty((Mn, Nn), dtype=torch.int16, device=dev)
     Sa, Sw = 0.002, 0.0005
 
-    def go(i):
-        bd.svdq_quantize_act(cfg, Mn, x, si, l1, Sa, ac, asb, lora, sp)
+    def quant(i, st=sp):
+        bd.svdq_quantize_act(cfg, Mn, x, si, l1, Sa, ac, asb, lora, st)
+
+    def gemm(i, st=sp):
         bd.svdq_gemm_w4a4(cfg, Mn, ac, asb, Sa, wc, ws, Sw, lora, l2, bias, bd.SVDQ_ACT_NONE,
-                          bd.SVDQ_DT_BF16, out, sp)
+                          bd.SVDQ_DT_BF16, out, st)
+
+    def go(i, st=sp):
+        quant(i, st)
+        gemm(i, st)
 
     go(0)
     torch.cuda.synchronize()
-    n = max(3, steps // 5)
-    ms = time_launches(go, n, stream)
+    stl = launch_stats(go, 5, reps)
+    stg = launch_stats(gemm, 5, reps)
+    ms, msg = stl["mean"], stg["mean"]
     ops = 2.0 * Mn * Nn * Kn + 2.0 * Mn * Nn * Rn + 2.0 * Mn * Kn * Rn
+    ops_g = 2.0 * Mn * Nn * Kn + 2.0 * Mn * Nn * Rn
     tops = ops / (ms * 1e-3) / 1e12
+    tops_g = ops_g / (msg * 1e-3) / 1e12
     return {"workload": "nvfp4_qkv_4096x3072x9216_r32", "ms_per_linear": round(ms, 4),
+            "ms_median": stl["median"], "ms_p10": stl["p10"], "ms_p90": stl["p90"], "reps": reps,
             "TOPS": round(tops, 2), "bf16_peak_frac": round(tops / BF16_PEAK_TFLOPS, 4),
-            "fp4_peak_frac": round(tops / FP4_PEAK_TFLOPS, 4)}
+            "fp4_peak_frac": round(tops / FP4_PEAK_TFLOPS, 4),
+            "gemm_ms": round(msg, 4), "gemm_ms_median": stg["median"], "gemm_TOPS": round(tops_g, 2),
+            "gemm_f16_peak_frac": round(tops_g / BF16_PEAK_TFLOPS, 4)}
 
 
-def mlp_leg(steps, sp, stream):
+def mlp_leg(reps, sp, stream):
     """DiT MLP block on the packed path (M=4608 tokens, 3072 -> 12288 -> 3072, rank 32):
     fc1 with GELU(tanh) in its epilogue writing bf16, then fc2's activation kernel reads that
-    output and fc2 writes fp32; and the same block with fc2's activation kernel fused into
-    fc1's epilogue (the bf16 intermediate never stored).  Weights are this library's own quantization of bf16
-    N(0, 0.02) draws; activations bf16 N(0, 1) with 31 outlier channels x50."""
+    output and fc2 writes fp32 (its nearly empty last round of tiles split over K in the
+    workspace); and the same block with fc2's activation kernel fused into fc1's epilogue
+    (the bf16 intermediate never stored).  Weights are this library's own quantization of
+    bf16 N(0, 0.02) draws; activations bf16 N(0, 1) with 31 outlier channels x50."""
     import torch
     import bit_diffusion_amd as bd
     Mm, K1, N1, Rm = 4608, 3072, 12288, 32
@@ -236,33 +292,42 @@ def mlp_leg(steps, sp, stream):
     x.view(torch.bfloat16)[:, torch.randperm(K1, device=dev, generator=g)[:31]] *= 50
     h = torch.empty((Mm, N1), dtype=torch.int16, device=dev)
     y = torch.empty((Mm, N2), dtype=torch.float32, device=dev)
+    split_bytes = bd.svdq_gemm_w4a4_packed_workspace_bytes(fc2["cfg"], Mm, bd.SVDQ_ACT_NONE,
+                                                           bd.SVDQ_DT_F32)
+    split_ws = torch.empty(max(split_bytes, 16), dtype=torch.uint8, device=dev)
+    work = torch.empty(bd.svdq_quantize_next_workspace_bytes(fc1["cfg"], fc2["cfg"], Mm) // 4,
+                       dtype=torch.float32, device=dev)
 
-    def quant(L, a):
-        bd.svdq_quantize_act_packed(L["cfg"], Mm, a, L["si"], L["l1p"], L["apk"], None, L["lora"], sp)
+    def quant(L, a, st):
+        bd.svdq_quantize_act_packed(L["cfg"], Mm, a, L["si"], L["l1p"], L["apk"], None, L["lora"], st)
 
-    def gemm(L, act, dt, out):
-        bd.svdq_gemm_w4a4_packed(L["cfg"], Mm, L["apk"], L["packed"], L["lora"], L["l2"], L["bias"],
-                                 act, dt, out, sp)
+    def gemm1(i, st=sp):
+        bd.svdq_gemm_w4a4_packed(fc1["cfg"], Mm, fc1["apk"], fc1["packed"], fc1["lora"], fc1["l2"],
+                                 fc1["bias"], bd.SVDQ_ACT_GELU_TANH, bd.SVDQ_DT_BF16, h, st)
 
-    def go(i):
-        quant(fc1, x)
-        gemm(fc1, bd.SVDQ_ACT_GELU_TANH, bd.SVDQ_DT_BF16, h)
-        quant(fc2, h)
-        gemm(fc2, bd.SVDQ_ACT_NONE, bd.SVDQ_DT_F32, y)
+    def gemm2(out, st):
+        bd.svdq_gemm_w4a4_packed_ws(fc2["cfg"], Mm, fc2["apk"], fc2["packed"], fc2["lora"], fc2["l2"],
+                                    fc2["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_F32, out, split_ws,
+                                    split_bytes, st)
 
-    work = torch.empty((Mm, Rm), dtype=torch.float32, device=dev)
+    def go(i, st=sp):
+        quant(fc1, x, st)
+        gemm1(i, st)
+        quant(fc2, h, st)
+        gemm2(y, st)
+
     yf = torch.empty_like(y)
 
-    def fc1_fused():
+    def fc1_fused(i, st=sp):
         bd.svdq_gemm_w4a4_packed_quantize_next(
             fc1["cfg"], Mm, fc1["apk"], fc1["packed"], fc1["lora"], fc1["l2"], fc1["bias"],
             bd.SVDQ_ACT_GELU_TANH, fc2["cfg"], fc2["si"], fc2["l1"], fc2["apk"], None, fc2["lora"],
-            work, sp)
+            work, st)
 
-    def go_fused(i):   # fc2's activation kernel runs inside fc1's GEMM epilogue
-        quant(fc1, x)
-        fc1_fused()
-        gemm(fc2, bd.SVDQ_ACT_NONE, bd.SVDQ_DT_F32, yf)
+    def go_fused(i, st=sp):   # fc2's activation kernel runs inside fc1's GEMM epilogue
+        quant(fc1, x, st)
+        fc1_fused(i, st)
+        gemm2(yf, st)
 
     go(0)
     go_fused(0)
@@ -271,24 +336,29 @@ def mlp_leg(steps, sp, stream):
     fused_rel = float((yf - y).double().norm() / y.double().norm())
     if not fused_rel <= 1e-3:
         raise RuntimeError(f"fused MLP differs from the unfused block: rel {fused_rel:.3e}")
-    n = max(3, steps // 5)
-    ms = time_launches(go, n, stream)
-    ms_fused = time_launches(go_fused, n, stream)
-    ms_fc1 = time_launches(lambda i: gemm(fc1, bd.SVDQ_ACT_GELU_TANH, bd.SVDQ_DT_BF16, h), n, stream)
-    ms_fc1f = time_launches(lambda i: fc1_fused(), n, stream)
-    ms_q2 = time_launches(lambda i: quant(fc2, h), n, stream)
+    st = launch_stats(go, 3, reps)
+    stf = launch_stats(go_fused, 3, reps)
+    ms, ms_fused = st["mean"], stf["mean"]
+    ms_fc1 = launch_stats(gemm1, 3, reps)["mean"]
+    ms_fc1f = launch_stats(fc1_fused, 3, reps)["mean"]
+    ms_q2 = launch_stats(lambda i, s_: quant(fc2, h, s_), 3, reps)["mean"]
+    ms_fc2 = launch_stats(lambda i, s_: gemm2(y, s_), 3, reps)["mean"]
     ops1 = 2.0 * Mm * N1 * K1 + 2.0 * Mm * N1 * Rm
     ops2 = 2.0 * Mm * N2 * K2 + 2.0 * Mm * N2 * Rm
     ops = ops1 + ops2 + 2.0 * Mm * (K1 + K2) * Rm
     tops = ops / (ms * 1e-3) / 1e12
     q2_bytes = Mm * K2 * 2 + bd.svdq_act_packed_bytes(fc2["cfg"], Mm) + Mm * Rm * 2 + Rm * K2 * 2
     return {"workload": "mlp_4608x3072x12288x3072_r32", "ms_per_mlp": round(ms, 4),
+            "ms_median": st["median"], "ms_p10": st["p10"], "ms_p90": st["p90"], "reps": reps,
             "TOPS": round(tops, 2), "pct_of_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
             "fc1_gelu_bf16_gemm_ms": round(ms_fc1, 4),
             "fc1_gelu_bf16_gemm_TOPS": round(ops1 / (ms_fc1 * 1e-3) / 1e12, 2),
             "fc2_quantize_ms": round(ms_q2, 4),
             "fc2_quantize_GBs": round(q2_bytes / (ms_q2 * 1e-3) / 1e9, 1),
-            "ms_per_mlp_fused": round(ms_fused, 4),
+            "fc2_gemm_ksplit_ms": round(ms_fc2, 4),
+            "fc2_gemm_ksplit_TOPS": round(ops2 / (ms_fc2 * 1e-3) / 1e12, 2),
+            "fc2_split_workspace_bytes": split_bytes,
+            "ms_per_mlp_fused": round(ms_fused, 4), "fused_ms_median": stf["median"],
             "fused_TOPS": round(ops / (ms_fused * 1e-3) / 1e12, 2),
             "fc1_gemm_quantize_next_ms": round(ms_fc1f, 4),
             "fused_vs_unfused_rel": float(f"{fused_rel:.3e}")}
@@ -344,7 +414,7 @@ def weights_leg(steps, sp, stream):
             "lowrank_factors_ms": round(ms_f, 3), "lowrank_block": Bw, "lowrank_iters": It}
 
 
-def lora_leg(steps, sp, stream, si, sets):
+def lora_leg(reps, sp, stream, si, sets):
     """The attention projection with a rank-16 LoRA adapter merged into its low-rank branch
     (svdq_merge_lora: rank 32 + 16 = 48), eager launches over the same rotating inputs."""
     import torch
@@ -367,20 +437,22 @@ def lora_leg(steps, sp, stream, si, sets):
         bd.svdq_prepack_l1(cfgm, l1m, l1p)
         merged.append(dict(l1p=l1p, l2=l2m, lora=torch.empty((M, ro), dtype=torch.int16, device=dev)))
 
-    def go(i):
+    def go(i, st=sp):
         s, m = sets[i % len(sets)], merged[i % len(sets)]
         bd.svdq_quantize_act_packed(cfgm, M, s["x"], si, m["l1p"], s["apacked"], s["scales"],
-                                    m["lora"], sp)
+                                    m["lora"], st)
         bd.svdq_gemm_w4a4_packed(cfgm, M, s["apacked"], s["packed"], m["lora"], m["l2"],
-                                 s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16, s["out"], sp)
+                                 s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16, s["out"], st)
 
     for i in range(len(sets)):
         go(i)
     torch.cuda.synchronize()
-    ms = time_launches(go, steps, stream)
+    st = launch_stats(go, len(sets), reps)
+    ms = st["mean"]
     ops = 2.0 * M * N * K + 2.0 * M * N * ro + 2.0 * M * K * ro
     return {"workload": f"attn_4096x3072x3072_r{R}+lora{rl}", "merged_rank": ro,
-            "ms_per_step_eager": round(ms, 5), "TOPS": round(ops / (ms * 1e-3) / 1e12, 2)}
+            "ms_per_step": round(ms, 5), "ms_median": st["median"], "reps": reps,
+            "TOPS": round(ops / (ms * 1e-3) / 1e12, 2)}
 
 
 def make_inputs(copies):
@@ -440,9 +512,32 @@ def make_inputs(copies):
     return si, sets, d
 
 
-def cpu_baseline(rows):
-    """The CPU oracle (single thread, as it stands) on the first `rows` token rows of the
-    same workload: activation stage + GEMM with the low-rank branch and bias."""
+def host_cpu():
+    """(CPU model name, logical CPUs this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    return model, ncpu
+
+
+def cpu_baseline(rows, threads, single_rows):
+    """The CPU oracle (as it stands: plain scalar C, one call per row block) on the first
+    `rows` token rows of the same workload: activation stage + GEMM with the low-rank branch
+    and bias.  The rows are cut into `threads` blocks run by as many host threads (the
+    oracle's C calls release the interpreter lock), so every core works; the first
+    `single_rows` rows also run on one thread, for the per-core figure."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     import synth
 
@@ -456,14 +551,69 @@ def cpu_baseline(rows):
     wc = synth.random_packed_nibbles(rng, N, K)
     ws = rng.uniform(0.001, 0.1, (N, K // 64)).astype(np.float32)
     oracle.lib()
+
+    def block(lo, hi):
+        c, s, lo_act = oracle.quant_act_int4(np.ascontiguousarray(xb[lo:hi]), si, l1)
+        oracle.gemm_w4a4_int4(c, s, wc, ws, lo_act, l2, d.bias_bf16)
+
+    def ops_of(n):
+        return 2.0 * n * N * K + 2.0 * n * N * R + 2.0 * n * K * R
+
     t0 = time.perf_counter()
-    c, s, lo = oracle.quant_act_int4(xb, si, l1)
-    oracle.gemm_w4a4_int4(c, s, wc, ws, lo, l2, d.bias_bf16)
+    block(0, single_rows)
+    t1 = time.perf_counter() - t0
+    edges = np.linspace(0, rows, threads + 1).astype(int)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda i: block(edges[i], edges[i + 1]), range(threads)))
     dt = time.perf_counter() - t0
-    ops = 2.0 * rows * N * K + 2.0 * rows * N * R + 2.0 * rows * K * R
-    return dict(value=ops / dt / 1e12, unit="TOPS", cores=1, kind="oracle",
-                sample=f"{rows} of {M} token rows, full K and N, single-threaded C oracle, "
-                       f"{dt:.1f} s")
+    model, ncpu = host_cpu()
+    return dict(value=ops_of(rows) / dt / 1e12, unit="TOPS", cores=threads, kind="oracle",
+                sample=f"{rows} of {M} token rows, full K and N, C oracle on {threads} host "
+                       f"threads, {dt:.2f} s wall",
+                cpu_model=model, nproc=ncpu,
+                single_thread={"value": ops_of(single_rows) / t1 / 1e12, "unit": "TOPS",
+                               "rows": single_rows, "seconds": round(t1, 2)})
+
+
+def peaks_leg(sp, stream):
+    """Measured denominators: each MFMA kind of the kernels at its sustained rate (a kernel
+    with independent back-to-back MFMAs on every SIMD, operands in registers), and a plain
+    copy through HBM (512 MiB each way, median of 20)."""
+    import torch
+    import bit_diffusion_amd as bd
+    out = torch.zeros(4, dtype=torch.float32, device="cuda:0")
+    names = {0: "fp6_32x32x64", 1: "i8_32x32x32", 2: "bf16_32x32x16", 3: "bf16_32x32x8",
+             4: "f16_32x32x16", 5: "fp4_32x32x64"}
+    res = {}
+    for kind, name in names.items():
+        iters = 2048
+        bd.svdq_peak_mfma(kind, iters, out, sp)          # warm
+        torch.cuda.synchronize()
+        best = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ops = bd.svdq_peak_mfma(kind, iters, out, sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best.append(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res[name] = round(float(np.median(best)), 1)
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    bd.svdq_peak_copy(src, dst, n, sp)
+    torch.cuda.synchronize()
+    gbs = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bd.svdq_peak_copy(src, dst, n, sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbs.append(2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return {"mfma_TOPS": res, "copy_GBs": round(float(np.median(gbs)), 1)}
 
 
 def main():
@@ -479,10 +629,18 @@ def main():
         copy_calibration()
         return
     assert bd.svdq_check_device(0) == bd.SVDQ_OK, bd.svdq_last_error()
-    si, sets, _ = make_inputs(args.copies)
-    cfg = bd.LayerCfg.make(K, N, R)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    if args.leg is not None:   # one leg alone (for profiling runs)
+        legs = {"awq": lambda: awq_leg(args.reps, sp, stream),
+                "nvfp4": lambda: nvfp4_leg(args.reps, sp, stream),
+                "mlp": lambda: mlp_leg(args.reps, sp, stream),
+                "weights": lambda: weights_leg(args.steps, sp, stream),
+                "peaks": lambda: peaks_leg(sp, stream)}
+        print(json.dumps({args.leg: legs[args.leg]()}), flush=True)
+        return
+    si, sets, _ = make_inputs(args.copies)
+    cfg = bd.LayerCfg.make(K, N, R)
 
     def quant(s, st=sp):
         bd.svdq_quantize_act_packed(cfg, M, s["x"], si, s["l1p"], s["apacked"], s["scales"],
@@ -511,7 +669,8 @@ def main():
 
     # whole-step timing: the `steps` steps captured once into a HIP graph (capturing runs
     # nothing) and replayed, as a denoising loop launches its layers; one untimed replay
-    # first (the graph's first launch uploads it)
+    # first (the graph's first launch uploads it), then one timed replay: exactly `steps`
+    # steps between a synchronisation and an event pair on the replaying stream
     cs = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(cs):
@@ -534,23 +693,34 @@ def main():
     torch.cuda.synchronize()
     if not torch.equal(from_graph, sets[j]["out"]):
         raise RuntimeError("graph replay and eager launch disagree")
+    # the spread: `reps` more timed replays of the same graph
+    reps_t = []
+    for _ in range(args.reps):
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        reps_t.append(ev0.elapsed_time(ev1) / args.steps)
+    reps_t = np.array(reps_t)
 
-    # per-kernel timing: each kernel launched `steps` times back to back over the rotating
-    # input sets, one event pair around the batch on the launching stream (an event pair
-    # around every launch would add the event packets' own latency to each kernel)
-    t_q = np.array(time_launches(lambda i: quant(sets[i % len(sets)]), args.steps, stream))
-    t_g = np.array(time_launches(lambda i: gemm(sets[i % len(sets)]), args.steps, stream))
+    # per-kernel timing: each kernel alone, `steps` launches back to back over the rotating
+    # input sets captured in a graph, replayed `reps` times with an event pair around each
+    # replay on the launching stream
+    st_q = launch_stats(lambda i, st: quant(sets[i % len(sets)], st), args.steps, args.reps)
+    st_g = launch_stats(lambda i, st: gemm(sets[i % len(sets)], st), args.steps, args.reps)
 
     ops_gemm = 2.0 * M * N * K + 2.0 * M * N * R
     ops_total = ops_gemm + 2.0 * M * K * R
     value = ops_total / (ms_step * 1e-3) / 1e12
-    gemm_tops = ops_gemm / (t_g.mean() * 1e-3) / 1e12
+    gemm_tops = ops_gemm / (st_g["mean"] * 1e-3) / 1e12
     # read x, smooth_inv, L1; write 6-bit codes + a 4-byte scale word per (row, group), the
     # fp32 scales and lora_act
     quant_bytes = (M * K * 2 + K * 4 + R * K * 2 + M * K * 3 // 4 + M * (K // 64) * 8
                    + M * R * 2)
-    quant_gbs = quant_bytes / (t_q.mean() * 1e-3) / 1e9
+    quant_gbs = quant_bytes / (st_q["mean"] * 1e-3) / 1e9
     traffic = recorded_traffic()
+    peaks = peaks_leg(sp, stream)
+    mfma_meas = peaks["mfma_TOPS"]
 
     out = {
         "metric": "W4A4+low-rank r32 linear TOPS @4096x3072x3072; % of int8 MFMA peak",
@@ -560,6 +730,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_stats": {"median": round(float(np.median(reps_t)), 5),
+                              "p10": round(float(np.percentile(reps_t, 10)), 5),
+                              "p90": round(float(np.percentile(reps_t, 90)), 5),
+                              "reps": args.reps, "steps_per_rep": args.steps},
         "ms_per_step_eager": round(ms_eager, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -572,23 +746,33 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
                      "traffic": traffic, "kernel": "svdq_gemm_w4a4_packed (int4 as FP6 on the MFMA)",
-                     "ms_per_launch": round(float(t_g.mean()), 5)},
+                     "ms_per_launch": st_g["mean"], "launch_stats": st_g,
+                     "frac_of_fp6_peak": round(gemm_tops / FP4_PEAK_TFLOPS, 4),
+                     "measured_peaks_TOPS": {"i8": mfma_meas["i8_32x32x32"],
+                                             "fp6": mfma_meas["fp6_32x32x64"]},
+                     "frac_of_measured_i8": round(gemm_tops / mfma_meas["i8_32x32x32"], 4)},
         "kernels": {
-            "quantize_act_ms": round(float(t_q.mean()), 5),
+            "quantize_act_ms": st_q["mean"],
+            "quantize_act_stats": st_q,
             "quantize_act_GBs": round(quant_gbs, 1),
             "quantize_act_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4),
-            "gemm_ms": round(float(t_g.mean()), 5),
+            "quantize_act_copy_frac": round(quant_gbs / peaks["copy_GBs"], 4),
+            "gemm_ms": st_g["mean"],
             "gemm_TOPS": round(gemm_tops, 2),
         },
+        "peaks_measured": peaks,
     }
     if not args.only_main:
-        out["awq"] = awq_leg(args.steps, sp, stream)
-        out["nvfp4"] = nvfp4_leg(args.steps, sp, stream)
-        out["mlp"] = mlp_leg(args.steps, sp, stream)
-        out["lora"] = lora_leg(args.steps, sp, stream, si, sets)
+        out["awq"] = awq_leg(args.reps, sp, stream)
+        out["awq"]["copy_frac"] = round(out["awq"]["GBs"] / peaks["copy_GBs"], 4)
+        out["nvfp4"] = nvfp4_leg(args.reps, sp, stream)
+        out["mlp"] = mlp_leg(args.reps, sp, stream)
+        out["lora"] = lora_leg(args.reps, sp, stream, si, sets)
         out["weights"] = weights_leg(args.steps, sp, stream)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+        model, ncpu = host_cpu()
+        threads = args.cpu_threads or max(1, min(16, ncpu))
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows, threads, args.single_rows)
     print(json.dumps(out), flush=True)
 
 

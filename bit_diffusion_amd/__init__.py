@@ -22,6 +22,8 @@ __all__ = [
     "svdq_prepacked_l1_bytes", "svdq_prepack_l1", "svdq_merged_rank", "svdq_merge_lora",
     "svdq_gemm_w4a4_packed_quantize_next", "svdq_calib_absmax", "svdq_smoothing_factors",
     "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
+    "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
+    "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -133,6 +135,28 @@ def svdq_gemm_w4a4_packed(cfg, M, act_packed, prepacked, lora_act, l2, bias, act
         _ptr(bias), int(act), int(out_dtype), _ptr(out), _stream(stream)))
 
 
+def svdq_gemm_w4a4_packed_workspace_bytes(cfg, M, act, out_dtype):
+    n = ctypes.c_int64(0)
+    _check(lib().svdq_gemm_w4a4_packed_workspace_bytes(ctypes.byref(cfg), int(M), int(act),
+                                                       int(out_dtype), ctypes.byref(n)))
+    return n.value
+
+
+def svdq_gemm_w4a4_packed_ws(cfg, M, act_packed, prepacked, lora_act, l2, bias, act, out_dtype, out,
+                             workspace, workspace_bytes, stream=None):
+    return _check(lib().svdq_gemm_w4a4_packed_ws(
+        ctypes.byref(cfg), int(M), _ptr(act_packed), _ptr(prepacked), _ptr(lora_act), _ptr(l2),
+        _ptr(bias), int(act), int(out_dtype), _ptr(out), _ptr(workspace), int(workspace_bytes),
+        _stream(stream)))
+
+
+def svdq_quantize_next_workspace_bytes(cfg, next_cfg, M):
+    n = ctypes.c_int64(0)
+    _check(lib().svdq_quantize_next_workspace_bytes(ctypes.byref(cfg), ctypes.byref(next_cfg),
+                                                    int(M), ctypes.byref(n)))
+    return n.value
+
+
 def svdq_gemm_w4a4_packed_quantize_next(cfg, M, act_packed, prepacked, lora_act, l2, bias, act,
                                         next_cfg, next_smooth_inv, next_l1, next_act_packed,
                                         next_act_scales, next_lora_act, lora_workspace,
@@ -171,6 +195,17 @@ def svdq_lowrank_factors(cfg, w, smooth_inv, omega, block, iters, l1, l2, sigma,
     return _check(lib().svdq_lowrank_factors(ctypes.byref(cfg), _ptr(w), _ptr(smooth_inv),
                                              _ptr(omega), int(block), int(iters), _ptr(l1), _ptr(l2),
                                              _ptr(sigma), _ptr(workspace), _stream(stream)))
+
+
+def svdq_peak_mfma(kind, iters, out, stream=None):
+    """Launch the MFMA-rate kernel of `kind`; returns the operations the launch performs."""
+    n = ctypes.c_int64(0)
+    _check(lib().svdq_peak_mfma(int(kind), int(iters), _ptr(out), ctypes.byref(n), _stream(stream)))
+    return n.value
+
+
+def svdq_peak_copy(src, dst, nbytes, stream=None):
+    return _check(lib().svdq_peak_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)))
 
 
 def svdq_check_device(device=0):

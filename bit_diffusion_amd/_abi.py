@@ -21,14 +21,16 @@ SVDQ_DT_BF16 = 1
 SVDQ_ACT_NONE = 0
 SVDQ_ACT_GELU_TANH = 1
 
-# Every symbol include/svdq.h declares.
+# Every symbol include/*.h declares.
 EXPORTS = ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_device",
            "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version",
            "svdq_act_packed_bytes", "svdq_prepacked_weight_bytes", "svdq_quantize_act_packed",
            "svdq_pack_act", "svdq_prepack_weight", "svdq_gemm_w4a4_packed",
            "svdq_prepacked_l1_bytes", "svdq_prepack_l1", "svdq_merged_rank", "svdq_merge_lora",
            "svdq_gemm_w4a4_packed_quantize_next", "svdq_calib_absmax", "svdq_smoothing_factors",
-           "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors")
+           "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
+           "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
+           "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy")
 
 
 class LayerCfg(ctypes.Structure):
@@ -85,6 +87,13 @@ def lib():
         L.svdq_lowrank_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_int64)]
         L.svdq_lowrank_factors.argtypes = [cfgp, P, P, P, I32, I32, P, P, P, P, P]
         L.svdq_gemm_w4a4_packed.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P]
+        L.svdq_gemm_w4a4_packed_workspace_bytes.argtypes = [cfgp, I64, I32, I32,
+                                                            ctypes.POINTER(ctypes.c_int64)]
+        L.svdq_gemm_w4a4_packed_ws.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P, I64, P]
+        L.svdq_quantize_next_workspace_bytes.argtypes = [cfgp, cfgp, I64,
+                                                         ctypes.POINTER(ctypes.c_int64)]
+        L.svdq_peak_mfma.argtypes = [I32, I32, P, ctypes.POINTER(ctypes.c_int64), P]
+        L.svdq_peak_copy.argtypes = [P, P, I64, P]
         L.svdq_check_device.argtypes = [ctypes.c_int]
         L.svdq_check_arch.argtypes = [ctypes.c_char_p]
         L.svdq_status_string.argtypes = [ctypes.c_int]
@@ -98,7 +107,9 @@ def lib():
                      "svdq_prepack_weight", "svdq_gemm_w4a4_packed", "svdq_prepacked_l1_bytes",
                      "svdq_prepack_l1", "svdq_merge_lora", "svdq_gemm_w4a4_packed_quantize_next",
                      "svdq_calib_absmax", "svdq_smoothing_factors", "svdq_quantize_residual",
-                     "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors"):
+                     "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
+                     "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
+                     "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/svdq.h"
+#include "../../include/svdq_peaks.h"
 #include "launch.hpp"
 #include "packed_layout.hpp"
 
@@ -338,10 +339,16 @@ svdq_status svdq_prepack_weight(const svdq_layer_cfg* cfg, const void* wgt_codes
     return after_launch("svdq_prepack_weight");
 }
 
-svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
-                                  const void* prepacked, const void* lora_act, const void* l2,
-                                  const void* bias, int32_t act, int32_t out_dtype, void* out,
-                                  svdq_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the packed GEMM entry points: validation, then the launch with the K-split
+// workspace `ws` of `ws_bytes` bytes (NULL: no K split).
+svdq_status gemm_packed(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
+                        const void* prepacked, const void* lora_act, const void* l2,
+                        const void* bias, int32_t act, int32_t out_dtype, void* out, void* ws,
+                        int64_t ws_bytes, svdq_stream_t stream, const char* name) {
     SVDQ_TRY(check_cfg(cfg));
     SVDQ_TRY(check_int4(cfg));
     if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
@@ -357,6 +364,8 @@ svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const vo
         SVDQ_TRY(check_ptr(l2, "l2", 16));
     }
     if (bias != nullptr && !aligned(bias, 2)) return fail(SVDQ_ERR_INVALID_ARG, "bias is not 2-byte aligned");
+    if (ws_bytes < 0) return fail(SVDQ_ERR_INVALID_ARG, "workspace_bytes = %lld is negative", (long long)ws_bytes);
+    if (ws != nullptr && !aligned(ws, 16)) return fail(SVDQ_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
     const int64_t tiles = ((M + 255) / 256) * ((cfg->out_features + 191) / 192);
     if (tiles >= (int64_t)1 << 31)
         return fail(SVDQ_ERR_UNSUPPORTED_CONFIG, "M = %lld too large for one launch", (long long)M);
@@ -366,8 +375,62 @@ svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const vo
         return fail(SVDQ_ERR_LAUNCH, "could not reserve LDS for the packed GEMM");
     svdq::PackedGemmArgs a{M, cfg->out_features, cfg->in_features, cfg->rank, act_packed,
                            prepacked, lora_act, l2, bias, act, out_dtype == SVDQ_DT_BF16 ? 1 : 0, out, 0};
+    a.split_ws = ws_bytes > 0 ? static_cast<float*>(ws) : nullptr;
+    a.split_ws_bytes = ws_bytes;
     svdq::launch_gemm_w4a4_fp6(a, reinterpret_cast<hipStream_t>(stream));
-    return after_launch("svdq_gemm_w4a4_packed");
+    return after_launch(name);
+}
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
+                                  const void* prepacked, const void* lora_act, const void* l2,
+                                  const void* bias, int32_t act, int32_t out_dtype, void* out,
+                                  svdq_stream_t stream) {
+    return gemm_packed(cfg, M, act_packed, prepacked, lora_act, l2, bias, act, out_dtype, out,
+                       nullptr, 0, stream, "svdq_gemm_w4a4_packed");
+}
+
+svdq_status svdq_gemm_w4a4_packed_workspace_bytes(const svdq_layer_cfg* cfg, int64_t M, int32_t act,
+                                                  int32_t out_dtype, int64_t* bytes) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    if (bytes == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "bytes is NULL");
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
+        return fail(SVDQ_ERR_INVALID_ARG, "act %d is not a svdq_act value", act);
+    if (out_dtype != SVDQ_DT_F32 && out_dtype != SVDQ_DT_BF16)
+        return fail(SVDQ_ERR_INVALID_ARG, "out_dtype %d is not a svdq_dtype value", out_dtype);
+    SVDQ_TRY(check_current_device());
+    *bytes = M == 0 ? 0
+                    : svdq::split_workspace_bytes(M, cfg->out_features, cfg->in_features, act,
+                                                  out_dtype == SVDQ_DT_BF16 ? 1 : 0);
+    return SVDQ_OK;
+}
+
+svdq_status svdq_gemm_w4a4_packed_ws(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
+                                     const void* prepacked, const void* lora_act, const void* l2,
+                                     const void* bias, int32_t act, int32_t out_dtype, void* out,
+                                     void* workspace, int64_t workspace_bytes, svdq_stream_t stream) {
+    if (workspace == nullptr && workspace_bytes > 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "workspace is NULL but workspace_bytes = %lld",
+                    (long long)workspace_bytes);
+    return gemm_packed(cfg, M, act_packed, prepacked, lora_act, l2, bias, act, out_dtype, out,
+                       workspace, workspace_bytes, stream, "svdq_gemm_w4a4_packed_ws");
+}
+
+svdq_status svdq_quantize_next_workspace_bytes(const svdq_layer_cfg* cfg, const svdq_layer_cfg* next_cfg,
+                                               int64_t M, int64_t* bytes) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    SVDQ_TRY(check_cfg(next_cfg));
+    SVDQ_TRY(check_int4(next_cfg));
+    if (bytes == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "bytes is NULL");
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    *bytes = svdq::quantize_next_workspace_bytes(M, cfg->out_features, next_cfg->rank);
+    return SVDQ_OK;
 }
 
 svdq_status svdq_gemm_w4a4_packed_quantize_next(
@@ -399,8 +462,8 @@ svdq_status svdq_gemm_w4a4_packed_quantize_next(
         return fail(SVDQ_ERR_INVALID_ARG, "next_act_scales is not 4-byte aligned");
     if (next_cfg->rank > 0) {
         SVDQ_TRY(check_ptr(next_l1, "next_l1", 16));
-        SVDQ_TRY(check_ptr(next_lora_act, "next_lora_act", 2));
-        SVDQ_TRY(check_ptr(lora_workspace, "lora_workspace", 4));
+        SVDQ_TRY(check_ptr(next_lora_act, "next_lora_act", 8));
+        SVDQ_TRY(check_ptr(lora_workspace, "lora_workspace", 16));
     }
     const int64_t tiles = ((M + 255) / 256) * ((cfg->out_features + 191) / 192);
     if (tiles >= (int64_t)1 << 31)
@@ -503,6 +566,30 @@ svdq_status svdq_lowrank_factors(const svdq_layer_cfg* cfg, const float* w, cons
     svdq::launch_lowrank_factors(cfg->out_features, cfg->in_features, r, block, iters, w, smooth_inv, omega,
                                  l1, l2, sigma, workspace, reinterpret_cast<hipStream_t>(stream));
     return after_launch("svdq_lowrank_factors");
+}
+
+svdq_status svdq_peak_mfma(int32_t kind, int32_t iters, float* out, int64_t* ops,
+                           svdq_stream_t stream) {
+    if (kind < 0 || kind > 5) return fail(SVDQ_ERR_INVALID_ARG, "kind %d is not in [0, 5]", kind);
+    if (iters < 1 || iters > (1 << 20)) return fail(SVDQ_ERR_INVALID_ARG, "iters %d not in [1, 2^20]", iters);
+    SVDQ_TRY(check_ptr(out, "out", 4));
+    if (ops == nullptr) return fail(SVDQ_ERR_INVALID_ARG, "ops is NULL");
+    SVDQ_TRY(check_current_device());
+    *ops = svdq::launch_mfma_peak(kind, iters, out, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_peak_mfma");
+}
+
+svdq_status svdq_peak_copy(const void* src, void* dst, int64_t bytes, svdq_stream_t stream) {
+    if (bytes <= 0 || bytes % 16 != 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "bytes = %lld must be a positive multiple of 16", (long long)bytes);
+    SVDQ_TRY(check_ptr(src, "src", 16));
+    SVDQ_TRY(check_ptr(dst, "dst", 16));
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+    if (s < d + (uintptr_t)bytes && d < s + (uintptr_t)bytes)
+        return fail(SVDQ_ERR_INVALID_ARG, "src and dst overlap");
+    SVDQ_TRY(check_current_device());
+    svdq::launch_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_peak_copy");
 }
 
 svdq_status svdq_check_device(int device) { return check_device_ordinal(device); }

@@ -28,7 +28,10 @@
 // 2 x 3 tiles of 32x32 (two waves per SIMD, whose MFMA and VALU work overlap).  Workgroup
 // ids are remapped so the workgroups an XCD runs at once cover a compact block of tiles and
 // share its L2.  With fp32 output and no activation, a last round of tiles that would fill
-// at most a quarter of the GPU is split over K, the splits adding into a zeroed tile.
+// at most a quarter of the GPU is split over K when the caller passes a workspace: each
+// split stores its partial tile there and a second kernel adds the splits in a fixed order.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "packed_layout.hpp"
@@ -525,9 +528,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
             }
         }
         // this tile's channels' share of the next layer's lora_act = x . l1^T for rows
-        // 32 w .. + 31 (two 16-row MFMA blocks), added into the zeroed fp32 workspace
+        // 32 w .. + 31 (two 16-row MFMA blocks), stored as this tile's fp32 partial sums
+        // (slot pid_n of the workspace); a second kernel adds the slots in a fixed order
         if (R2 > 0) {
             const int nks = 2 * ngr;   // 32-channel steps
+            const int64_t Mpad = (int64_t)num_m * kBM;
+            float* part = p.lora_work + ((int64_t)pid_n * Mpad + m0) * R2;
             uint4 av[2][6];
 #pragma unroll
             for (int rb2 = 0; rb2 < 2; ++rb2)
@@ -552,27 +558,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
                 for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int64_t rw = m0 + wave * 32 + rb2 * 16 + 4 * (lane >> 4) + i;
-                        if (rw < M) unsafeAtomicAdd(p.lora_work + rw * R2 + 16 * jb + (lane & 15), c[rb2][i]);
+                        const int rw = wave * 32 + rb2 * 16 + 4 * (lane >> 4) + i;   // tile row (padding rows too)
+                        part[(int64_t)rw * R2 + 16 * jb + (lane & 15)] = c[rb2][i];
                     }
             }
         }
         return;
     }
     if constexpr (!kBf16 && !kGelu) {
-        if (split >= 0) {   // a K split: add into the zeroed fp32 tile
+        if (split >= 0) {
+            // A K split: this split's fp32 partial tile goes to its workspace slot in the
+            // accumulators' own order (lane-contiguous 16-byte pieces); sum_splits_kernel
+            // adds the splits in order 0, 1, ... and stores the tile.
+            float* part = p.split_ws + ((int64_t)(blockIdx.x - p.nfull)) * (kBM * kBN);
 #pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const int col = n0 + wn * 96 + j * 32 + fr;
-                if (col >= N) continue;
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int j = 0; j < 3; ++j)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-                        if (row < M) unsafeAtomicAdd((float*)p.out + row * N + col, acc[i][j][e]);
-                    }
-            }
+                    for (int e4 = 0; e4 < 4; ++e4)
+                        *reinterpret_cast<f32x4*>(part + ((((wave * 2 + i) * 3 + j) * 4 + e4) * 64 + lane) * 4) =
+                            f32x4{acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
             return;
         }
     }
@@ -711,42 +717,55 @@ bool set_lds_attr() {
                                hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes) == hipSuccess;
 }
 
-// Zero fp32 output tiles t >= nfull (those summed over K splits): workgroup b clears rows
-// 16 (b % 16) .. + 15 of tile nfull + b / 16, with 16-byte stores when rows allow them.
-__global__ __launch_bounds__(256) void zero_tiles_kernel(float* __restrict__ out, int64_t M, int N,
-                                                         int nfull, int vec) {
+// The K-split tiles t >= nfull: out = sum over splits s = 0, 1, ... of the partial tiles in
+// workspace slots (t - nfull) * nsplit + s, added in that order (bit-reproducible).  Block b
+// takes 256 of the 12288 16-byte pieces of tile nfull + b / 48; a piece holds four rows of
+// one column (the accumulators' order, see the kernel's K-split store).
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ ws,
+                                                         float* __restrict__ out, int64_t M, int N,
+                                                         int nfull, int nsplit) {
     const int num_m = (int)((M + kBM - 1) / kBM), num_n = (N + kBN - 1) / kBN;
+    const int u = blockIdx.x / 48;
     int pid_m, pid_n;
-    tile_of(nfull + (int)(blockIdx.x >> 4), pid_m, pid_n, num_m, num_n);
-    const int64_t r0 = (int64_t)pid_m * kBM + 16 * (blockIdx.x & 15);
-    const int c0 = pid_n * kBN;
-    if (vec) {   // N % 4 == 0 and a 16-byte aligned output
+    tile_of(nfull + u, pid_m, pid_n, num_m, num_n);
+    const int f = (blockIdx.x % 48) * 256 + threadIdx.x;   // piece in the tile
+    const int lane = f & 63, e4 = (f >> 6) & 3, j = (f >> 8) % 3, i = (f / 768) & 1, wave = f / 1536;
+    const float* src = ws + (int64_t)u * nsplit * (kBM * kBN) + 4 * f;
+    f32x4 v = *reinterpret_cast<const f32x4*>(src);
+    for (int s = 1; s < nsplit; ++s) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(src + (int64_t)s * (kBM * kBN));
+        v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+    }
+    const int col = pid_n * kBN + (wave & 1) * 96 + j * 32 + (lane & 31);
+    const int64_t row0 = (int64_t)pid_m * kBM + (wave >> 1) * 64 + i * 32 + 8 * e4 + 4 * (lane >> 5);
+    if (col < N) {
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int idx = threadIdx.x + 256 * k;   // 16 rows x 48 float4
-            const int64_t row = r0 + idx / 48;
-            const int col = c0 + 4 * (idx % 48);
-            if (row < M && col < N)
-                *reinterpret_cast<float4*>(out + row * N + col) = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    } else {
-        for (int idx = threadIdx.x; idx < 16 * kBN; idx += 256) {
-            const int64_t row = r0 + idx / kBN;
-            const int col = c0 + idx % kBN;
-            if (row < M && col < N) out[row * N + col] = 0.0f;
-        }
+        for (int k = 0; k < 4; ++k)
+            if (row0 + k < M) out[(row0 + k) * N + col] = v[k];
     }
 }
 
-__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
-}
-
-// fp32 low-rank sums -> bf16 lora_act (round to nearest even)
-__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src,
-                                                          uint16_t* __restrict__ dst, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        dst[i] = (uint16_t)f32_to_bf16(src[i]);
+// The next layer's lora_act from the fused epilogue's per-tile partial sums: lora[m, j] =
+// bf16(sum over column tiles t = 0, 1, ... of ws[t][m][j]) in that order, rounded once to
+// nearest even.  One thread per four consecutive ranks of a row.
+__global__ __launch_bounds__(256) void sum_lora_kernel(const float* __restrict__ ws,
+                                                       uint16_t* __restrict__ lora, int64_t M,
+                                                       int64_t Mpad, int R2, int ntn) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (m, 4 ranks)
+    const int q = R2 / 4;
+    if (idx >= M * q) return;
+    const int64_t m = idx / q;
+    const int j = 4 * (int)(idx % q);
+    const float* src = ws + m * R2 + j;
+    const int64_t stride = Mpad * R2;
+    f32x4 v = *reinterpret_cast<const f32x4*>(src);
+    for (int t = 1; t < ntn; ++t) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(src + t * stride);
+        v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+    }
+    const uint32_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    const uint32_t hi = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(lora + m * R2 + j) = make_uint2(lo, hi);
 }
 
 int cu_count() {
@@ -769,39 +788,65 @@ bool gemm_w4a4_fp6_init() {
     return ok == 1;
 }
 
+// Workspace of the K split: nsplit partial tiles for each of the `last` tiles of the last
+// round.  One tile per CU and round: when that round would be at most a quarter full, its
+// tiles are split over K so that it fills the GPU (fp32 output without GELU only), up to 8
+// splits of at least two groups, as many as kSplitWorkspaceMax and the caller's workspace
+// hold; with fewer than two splits there is no split.
+struct SplitPlan {
+    int nfull, nsplit, gsplit;
+};
+SplitPlan split_plan(int64_t M, int N, int K, int act_fn, int out_bf16, int64_t ws_bytes) {
+    const int num_m = (int)((M + kBM - 1) / kBM), num_n = (N + kBN - 1) / kBN;
+    const int nt = num_m * num_n, G = K >> 6;
+    SplitPlan sp{nt, 1, G};
+    const int ncu = cu_count();
+    const int last = nt % ncu;
+    if (out_bf16 || act_fn != 0 || nt <= ncu || last == 0 || 4 * last > ncu || G < 16) return sp;
+    const int64_t tile_bytes = (int64_t)kBM * kBN * 4;
+    const int64_t cap = std::min<int64_t>(ws_bytes, kSplitWorkspaceMax) / (tile_bytes * last);
+    int want = (int)std::min<int64_t>(std::min(8, ncu / last), cap);
+    if (want < 2) return sp;
+    sp.gsplit = (G + want - 1) / want;
+    sp.nsplit = (G + sp.gsplit - 1) / sp.gsplit;
+    sp.nfull = nt - last;
+    return sp;
+}
+
+int64_t split_workspace_bytes(int64_t M, int N, int K, int act_fn, int out_bf16) {
+    const SplitPlan sp = split_plan(M, N, K, act_fn, out_bf16, kSplitWorkspaceMax);
+    if (sp.nsplit < 2) return 0;
+    const int num_m = (int)((M + kBM - 1) / kBM), num_n = (N + kBN - 1) / kBN;
+    return (int64_t)(num_m * num_n - sp.nfull) * sp.nsplit * kBM * kBN * 4;
+}
+
+int64_t quantize_next_workspace_bytes(int64_t M, int N, int next_r) {
+    const int64_t Mpad = (M + kBM - 1) / kBM * kBM;
+    return (int64_t)((N + kBN - 1) / kBN) * Mpad * next_r * 4;
+}
+
 void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st) {
     const int num_m = (int)((a.M + kBM - 1) / kBM), num_n = (a.N + kBN - 1) / kBN;
-    const int nt = num_m * num_n, G = a.K >> 6;
+    const int nt = num_m * num_n;
     PackedGemmArgs b = a;
     const int esz = a.out_bf16 ? 2 : 4;
     b.vec_store = ((int64_t)a.N * esz) % 16 == 0 && (reinterpret_cast<uintptr_t>(a.out) % 16) == 0;
-    // One tile per CU and round: when the last round would be at most a quarter full, its
-    // tiles are split over K so that it fills the GPU (fp32 output without GELU only: the
-    // splits add into a zeroed tile; the sum order of the splits is not fixed).
-    b.nfull = nt;
-    b.nsplit = 1;
-    b.gsplit = G;
-    const int ncu = cu_count();
-    const int last = nt % ncu;
-    if (!a.quantize_next && !a.out_bf16 && a.act_fn == 0 && nt > ncu && last > 0 && 4 * last <= ncu &&
-        G >= 16) {
-        const int want = min(8, ncu / last);
-        b.gsplit = (G + want - 1) / want;
-        b.nsplit = (G + b.gsplit - 1) / b.gsplit;
-        b.nfull = nt - last;
-        hipLaunchKernelGGL(zero_tiles_kernel, dim3(16 * last), dim3(256), 0, st, (float*)a.out, a.M, a.N,
-                           b.nfull, b.vec_store);
-    }
+    const SplitPlan sp = a.quantize_next || a.split_ws == nullptr
+                             ? SplitPlan{nt, 1, a.K >> 6}
+                             : split_plan(a.M, a.N, a.K, a.act_fn, a.out_bf16, a.split_ws_bytes);
+    b.nfull = sp.nfull;
+    b.nsplit = sp.nsplit;
+    b.gsplit = sp.gsplit;
     const dim3 grid(b.nfull + (nt - b.nfull) * b.nsplit), block(kThreads);
-    if (a.quantize_next) {   // the next layer's low-rank sums: zeroed, added per tile, rounded
-        const int64_t nl = a.next_r > 0 ? a.M * a.next_r : 0;
-        const unsigned lb = (unsigned)std::min<int64_t>((nl + 255) / 256, 2048);
-        if (nl > 0) hipLaunchKernelGGL(zero_f32_kernel, dim3(lb), dim3(256), 0, st, a.lora_work, nl);
+    if (a.quantize_next) {   // the next layer's low-rank sums: per-tile partials, then summed
         if (a.act_fn == 1) hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, true, true>), grid, block, kSmemBytes, st, b);
         else hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, false, true>), grid, block, kSmemBytes, st, b);
-        if (nl > 0)
-            hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(lb), dim3(256), 0, st, (const float*)a.lora_work,
-                               (uint16_t*)a.out, nl);
+        if (a.next_r > 0) {
+            const int64_t n = a.M * (a.next_r / 4);
+            hipLaunchKernelGGL(sum_lora_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                               (const float*)a.lora_work, (uint16_t*)a.out, a.M, (int64_t)num_m * kBM,
+                               a.next_r, num_n);
+        }
         return;
     }
     if (a.out_bf16) {
@@ -811,6 +856,9 @@ void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st) {
         if (a.act_fn == 1) hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<false, true>), grid, block, kSmemBytes, st, b);
         else hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<false, false>), grid, block, kSmemBytes, st, b);
     }
+    if (b.nsplit > 1)
+        hipLaunchKernelGGL(sum_splits_kernel, dim3(48 * (nt - b.nfull)), dim3(256), 0, st,
+                           (const float*)a.split_ws, (float*)a.out, a.M, a.N, b.nfull, b.nsplit);
 }
 
 }  // namespace svdq

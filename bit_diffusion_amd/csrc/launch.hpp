@@ -70,8 +70,17 @@ struct PackedGemmArgs {
     const void* next_l1;     // bf16 [next_r, N] row-major, or NULL
     void* next_packed;       // the next layer's packed activation buffer (its K = N)
     float* next_scales;      // fp32 [M, N / 64] or NULL
-    float* lora_work;        // fp32 [M, next_r], zeroed: the next layer's low-rank sums
+    float* lora_work;        // fp32 [ceil(N / 192)][ceil(M / 256) * 256][next_r]: per-tile
+                             // partial sums of the next layer's low-rank down-projection
+    // K split (fp32 output, no activation): workspace for the splits' partial tiles, or NULL
+    // (then no split)
+    float* split_ws;
+    int64_t split_ws_bytes;
 };
+
+// Largest workspace the K split of svdq_gemm_w4a4_packed uses (its split count is capped so
+// that the partial tiles fit).
+constexpr int64_t kSplitWorkspaceMax = (int64_t)64 << 20;
 
 void launch_quantize_act(const QuantArgs& a, hipStream_t st);
 void launch_gemm_int4(const GemmArgs& a, hipStream_t st);
@@ -89,6 +98,13 @@ void launch_pack_act(int64_t M, int K, const void* acodes, const void* ascales, 
                      hipStream_t st);
 bool gemm_w4a4_fp6_init();
 void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st);
+int64_t split_workspace_bytes(int64_t M, int N, int K, int act_fn, int out_bf16);
+int cu_count();   // compute units of the current device (cached per device)
+
+// measurement kernels (peaks.hip)
+int64_t launch_mfma_peak(int kind, int iters, float* out, hipStream_t st);
+void launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+int64_t quantize_next_workspace_bytes(int64_t M, int N, int next_r);
 
 // offline weight quantization (weights.hip)
 void launch_calib_absmax(int64_t M, int K, const void* x, float* absmax, hipStream_t st);

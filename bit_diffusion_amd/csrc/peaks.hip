@@ -1,0 +1,143 @@
+// peaks.hip -- measurement kernels: the sustained rate of one MFMA kind with operands in
+// registers, and a plain HBM copy.  They are the measured denominators that a benchmark
+// reports beside the published MI355X peaks; nothing here is part of the method.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace svdq {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kPeakThreads = 512;   // 8 waves per CU: two per SIMD
+constexpr int kChains = 4;          // independent accumulators per wave
+
+template <int KIND>
+constexpr int64_t kOpsPerMfma = KIND == 0 || KIND == 5 ? 2 * 32 * 32 * 64
+                                : KIND == 1            ? 2 * 32 * 32 * 32
+                                : KIND == 3            ? 2 * 32 * 32 * 8
+                                                       : 2 * 32 * 32 * 16;
+
+// Operand words derived from the lane (so nothing folds to a constant) and kept small, so
+// the sums stay finite for any iteration count.
+__device__ __forceinline__ uint32_t seed_word(int lane, int e) {
+    return 0x01010101u * (uint32_t)((lane + 3 * e) & 3);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kPeakThreads) void mfma_peak_kernel(int iters, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    float total = 0.0f;
+    if constexpr (KIND == 0 || KIND == 5) {
+        constexpr int fmt = KIND == 0 ? 2 : 4;   // FP6 E2M3 or FP4 E2M1
+        i32x8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[e] = (int)seed_word(lane, e);
+            b[e] = (int)seed_word(lane + 1, e);
+        }
+        f32x16 c[kChains];
+#pragma unroll
+        for (int q = 0; q < kChains; ++q) c[q] = f32x16{};
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int q = 0; q < kChains; ++q)
+                c[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[q], fmt, fmt, 0, 127, 0, 127);
+#pragma unroll
+        for (int q = 0; q < kChains; ++q) total += c[q][0] + c[q][15];
+    } else if constexpr (KIND == 1) {
+        i32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (int)seed_word(lane, e);
+            b[e] = (int)seed_word(lane + 1, e);
+        }
+        i32x16 c[kChains];
+#pragma unroll
+        for (int q = 0; q < kChains; ++q) c[q] = i32x16{};
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int q = 0; q < kChains; ++q) c[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[q], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < kChains; ++q) total += (float)(c[q][0] + c[q][15]);
+    } else {
+        f32x16 c[kChains];
+#pragma unroll
+        for (int q = 0; q < kChains; ++q) c[q] = f32x16{};
+        const float v = 1.0f / (float)(1 + (lane & 7));
+        if constexpr (KIND == 2) {
+            bf16x8 a, b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                a[e] = (__bf16)(v * (float)e);
+                b[e] = (__bf16)(v + (float)e);
+            }
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int q = 0; q < kChains; ++q) c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[q], 0, 0, 0);
+        } else if constexpr (KIND == 3) {
+            bf16x4 a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = (__bf16)(v * (float)e);
+                b[e] = (__bf16)(v + (float)e);
+            }
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int q = 0; q < kChains; ++q) c[q] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c[q], 0, 0, 0);
+        } else {
+            f16x8 a, b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                a[e] = (_Float16)(v * (float)e);
+                b[e] = (_Float16)(v + (float)e);
+            }
+            for (int it = 0; it < iters; ++it)
+#pragma unroll
+                for (int q = 0; q < kChains; ++q) c[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c[q], 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < kChains; ++q) total += c[q][0] + c[q][15];
+    }
+    // a store that depends on every result, so no wave's MFMAs can be dropped
+    if (total == 1234.5f || threadIdx.x + blockIdx.x == 0) out[0] = total;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                   int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+template <int KIND>
+int64_t launch_peak(int iters, float* out, hipStream_t st) {
+    const int blocks = cu_count();
+    hipLaunchKernelGGL(mfma_peak_kernel<KIND>, dim3(blocks), dim3(kPeakThreads), 0, st, iters, out);
+    return (int64_t)blocks * (kPeakThreads / 64) * kChains * iters * kOpsPerMfma<KIND>;
+}
+
+}  // namespace
+
+int64_t launch_mfma_peak(int kind, int iters, float* out, hipStream_t st) {
+    switch (kind) {
+        case 0: return launch_peak<0>(iters, out, st);
+        case 1: return launch_peak<1>(iters, out, st);
+        case 2: return launch_peak<2>(iters, out, st);
+        case 3: return launch_peak<3>(iters, out, st);
+        case 4: return launch_peak<4>(iters, out, st);
+        default: return launch_peak<5>(iters, out, st);
+    }
+}
+
+void launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
+    const int64_t n = bytes / 16;
+    const int64_t want = (n + 255) / 256;
+    const unsigned blocks = (unsigned)std::min<int64_t>(want, (int64_t)cu_count() * 16);
+    hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, st, (const uint4*)src, (uint4*)dst, n);
+}
+
+}  // namespace svdq

@@ -179,11 +179,18 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
  * svdq_gemm_w4a4_packed: as svdq_gemm_w4a4 (INT4) on packed operands.  The result equals
  *   svdq_gemm_w4a4's up to fp32 rounding order and the three-term split of each scale
  *   product (relative error of one group's scale product a few fp32 ulp).  The output is
- *   computed in 256x192 tiles, one per compute unit at a time; with fp32 output and no
- *   activation, when the last round of tiles would fill at most a quarter of the compute
- *   units, those tiles are split over K and their partial sums added into the (first
- *   zeroed) output with fp32 atomics, so their values may differ in the last bits from run
- *   to run.  Every other case is bit-reproducible.
+ *   computed in 256x192 tiles, one per compute unit at a time, each summed over the groups
+ *   in a fixed order: the result is bit-reproducible from run to run.
+ * svdq_gemm_w4a4_packed_workspace_bytes: the workspace svdq_gemm_w4a4_packed_ws uses for
+ *   this layer, M rows, `act` and `out_dtype` (0 when it would not split; at most 64 MiB).
+ * svdq_gemm_w4a4_packed_ws: svdq_gemm_w4a4_packed with a caller-owned device workspace
+ *   (16-byte aligned, workspace_bytes long, contents overwritten; may be NULL with
+ *   workspace_bytes 0).  With fp32 output and no activation, when the last round of tiles
+ *   would fill at most a quarter of the compute units, those tiles are split over K into
+ *   up to 8 parts (as many as the workspace holds, at least 2, else no split): each part
+ *   stores its fp32 partial tile in the workspace and a second kernel adds the parts in the
+ *   fixed order of their K ranges.  Bit-reproducible from run to run for a given workspace
+ *   size; it differs from svdq_gemm_w4a4_packed's output only in the fp32 order of the sum.
  * All enqueue on `stream`.
  */
 svdq_status svdq_act_packed_bytes(const svdq_layer_cfg* cfg, int64_t M, int64_t* bytes);
@@ -203,6 +210,12 @@ svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const vo
                                   const void* prepacked, const void* lora_act, const void* l2,
                                   const void* bias, int32_t act, int32_t out_dtype, void* out,
                                   svdq_stream_t stream);
+svdq_status svdq_gemm_w4a4_packed_workspace_bytes(const svdq_layer_cfg* cfg, int64_t M, int32_t act,
+                                                  int32_t out_dtype, int64_t* bytes);
+svdq_status svdq_gemm_w4a4_packed_ws(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
+                                     const void* prepacked, const void* lora_act, const void* l2,
+                                     const void* bias, int32_t act, int32_t out_dtype, void* out,
+                                     void* workspace, int64_t workspace_bytes, svdq_stream_t stream);
 
 /* Two chained linears on the packed path with the second one's activation kernel fused into
  * the first one's GEMM (the DiT MLP: fc1 with GELU, then fc2).  The pages credit the original
@@ -219,12 +232,19 @@ svdq_status svdq_gemm_w4a4_packed(const svdq_layer_cfg* cfg, int64_t M, const vo
  * without the bf16 activations h [M, cfg->out_features] ever reaching memory: each output
  * tile is quantized in the GEMM's epilogue from the bf16 values it would store.  Codes,
  * scale words and next_act_scales are bit-identical to the unfused pair; next_lora_act
- * (bf16 [M, next rank]) is the same sum in another fp32 order (within one bf16 ulp; the
- * tiles' partial sums are added in no fixed order, so it is not bit-reproducible).
+ * (bf16 [M, next rank]) is the same sum in another fp32 order: each 192-column tile stores
+ * its fp32 partial sums in lora_workspace and a second kernel adds the tiles' partials in
+ * column order and rounds once, so it is bit-reproducible (and within one bf16 ulp of the
+ * unfused pair where the two fp32 sums straddle a rounding boundary).
  * next_cfg->in_features must equal cfg->out_features (both INT4).  next_l1 is the next
  * layer's row-major bf16 [rank, K] factor (not prepacked); lora_workspace is caller-owned
- * fp32 [M, next rank] scratch (overwritten).  next_act_scales may be NULL; next_l1,
+ * device scratch of svdq_quantize_next_workspace_bytes(cfg, next_cfg, M) bytes
+ * (ceil(N / 192) * ceil(M / 256) * 256 * next rank * 4; 16-byte aligned, overwritten);
+ * next_lora_act must be 8-byte aligned.  next_act_scales may be NULL; next_l1,
  * next_lora_act and lora_workspace may be NULL at next rank 0.  Enqueued on `stream`. */
+svdq_status svdq_quantize_next_workspace_bytes(const svdq_layer_cfg* cfg,
+                                               const svdq_layer_cfg* next_cfg, int64_t M,
+                                               int64_t* bytes);
 svdq_status svdq_gemm_w4a4_packed_quantize_next(
     const svdq_layer_cfg* cfg, int64_t M, const void* act_packed, const void* prepacked,
     const void* lora_act, const void* l2, const void* bias, int32_t act,

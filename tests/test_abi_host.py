@@ -1,5 +1,5 @@
 """Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
-include/svdq.h declares, and rejects bad arguments before touching any device."""
+the headers under include/ declare, and rejects bad arguments before touching any device."""
 import ctypes
 import os
 import re
@@ -9,15 +9,19 @@ import pytest
 import bit_diffusion_amd as bd
 from bit_diffusion_amd import _abi
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "svdq.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 
 def _declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text,
-                                 flags=re.M)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, h), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text,
+                                flags=re.M))
+    return sorted(names)
 
 
 def test_header_and_library_exports_agree():
@@ -210,3 +214,34 @@ def test_python_binding_raises_with_message():
     with pytest.raises(bd.SvdqError) as e:
         bd.svdq_quantize_act(cfg, 4, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == bd.SVDQ_ERR_INVALID_ARG and "in_features" in e.value.message
+
+
+def test_workspace_queries_and_rules():
+    """The fused MLP's workspace size is ceil(N / 192) column tiles x the rows padded to 256
+    x the next rank x 4 bytes; the K-split GEMM rejects a NULL workspace with a positive
+    size, a negative size and a misaligned workspace before touching the device."""
+    cfg = bd.LayerCfg.make(3072, 12288, 32)
+    ncfg = bd.LayerCfg.make(12288, 3072, 32)
+    assert bd.svdq_quantize_next_workspace_bytes(cfg, ncfg, 4608) == 64 * 4608 * 32 * 4
+    assert bd.svdq_quantize_next_workspace_bytes(cfg, ncfg, 300) == 64 * 512 * 32 * 4
+    assert bd.svdq_quantize_next_workspace_bytes(cfg, bd.LayerCfg.make(12288, 3072, 0), 300) == 0
+    odd = bd.LayerCfg.make(256, 448, 16)
+    assert bd.svdq_quantize_next_workspace_bytes(odd, bd.LayerCfg.make(448, 1, 16), 1) == 3 * 256 * 16 * 4
+    L = bd.lib()
+    n = ctypes.c_int64(0)
+    assert L.svdq_quantize_next_workspace_bytes(ctypes.byref(cfg), ctypes.byref(cfg), 10,
+                                                ctypes.byref(n)) == bd.SVDQ_OK
+    assert L.svdq_quantize_next_workspace_bytes(ctypes.byref(cfg), ctypes.byref(ncfg), -1,
+                                                ctypes.byref(n)) == bd.SVDQ_ERR_INVALID_ARG
+    f = L.svdq_gemm_w4a4_packed_ws
+    c = bd.LayerCfg.make(1024, 3072, 32)
+    args = (ctypes.byref(c), 4352, FAKE, FAKE, FAKE, FAKE, None, 0, bd.SVDQ_DT_F32, FAKE)
+    assert f(*args, None, 1024, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "workspace" in bd.svdq_last_error()
+    assert f(*args, FAKE, -16, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert f(*args, FAKE + 4, 1024, None) == bd.SVDQ_ERR_INVALID_ARG
+    assert "aligned" in bd.svdq_last_error()
+    assert L.svdq_gemm_w4a4_packed_workspace_bytes(ctypes.byref(c), -1, 0, 0,
+                                                   ctypes.byref(n)) == bd.SVDQ_ERR_INVALID_ARG
+    assert L.svdq_gemm_w4a4_packed_workspace_bytes(ctypes.byref(c), 10, 0, 0,
+                                                   None) == bd.SVDQ_ERR_INVALID_ARG

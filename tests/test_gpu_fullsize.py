@@ -67,9 +67,12 @@ def test_attn_projection_int4(workload_cache):
     e = gu.rel_fro(y[mi, ni], ref)
     print(f"attn int4 gemm rel_fro={e:.3e}")
     assert e <= 1e-3
+    K = d.x_bf16.shape[1]
+    cond = gu.int4_cond(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], L["bias"], mi, ni)
+    gu.assert_f32_within(y[mi, ni], ref, cond, gu.int4_nround(K, L["rank"]))
     yb = gu.host(gu.gemm(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], L["bias"],
                          out_bf16=True))
-    gu.assert_bf16_close(yb[mi, ni], ref)
+    gu.assert_bf16_close(yb[mi, ni], ref, cond, gu.int4_nround(K, L["rank"]))
     # end to end: GPU chain vs oracle chain from the same X
     ye = gu.host(gu.gemm(gc, gs, L["wcodes"], L["wscales"], gl, L["l2"], L["bias"]))
     e2e = gu.rel_fro(ye[mi, ni], ref)
@@ -88,7 +91,9 @@ def test_mlp_pair_int4(workload_cache):
     ref1 = oracle.gemm_w4a4_int4_at(mi1, ni1, oc1, os1, L1["wcodes"], L1["wscales"], ol1,
                                     L1["l2"], L1["bias"], act=1)
     # bf16 rounding alone is ~1.5e-3 relative: compare at the same rounding point
-    gu.assert_bf16_close(h_or[mi1, ni1], ref1)
+    cond1 = gu.int4_cond(oc1, os1, L1["wcodes"], L1["wscales"], ol1, L1["l2"], L1["bias"], mi1, ni1)
+    gu.assert_bf16_close(h_or[mi1, ni1], ref1, cond1, gu.int4_nround(d.x_bf16.shape[1], L1["rank"]),
+                         gelu=True)
     # the oracle's chain on a few token rows: fc1 -> GELU (fp64) -> bf16 -> fc2
     rows = np.array([0, 1, 777, 2048, 4095, d.x_bf16.shape[0] - 1])
     y1 = oracle.gemm_w4a4_int4(oc1[rows], os1[rows], L1["wcodes"], L1["wscales"], ol1[rows],
@@ -114,6 +119,8 @@ def test_mlp_pair_int4(workload_cache):
     e3 = gu.rel_fro(y3[mi3, ni3], ref3)
     print(f"mlp fc2 gemm rel_fro={e3:.3e}")
     assert e3 <= 1e-3
+    cond3 = gu.int4_cond(oc3, os3, L2["wcodes"], L2["wscales"], ol3, L2["l2"], L2["bias"], mi3, ni3)
+    gu.assert_f32_within(y3[mi3, ni3], ref3, cond3, gu.int4_nround(L2["wcodes"].shape[1] * 2, L2["rank"]))
 
 
 def test_qkv_nvfp4(workload_cache):
@@ -128,6 +135,13 @@ def test_qkv_nvfp4(workload_cache):
     e = gu.rel_fro(y[mi, ni], ref)
     print(f"qkv nvfp4 gemm rel_fro={e:.3e}")
     assert e <= 1e-3
+    cond = gu.nvfp4_cond(oc, os_, L["Sa"], L["wcodes"], L["wscales"], L["Sw"], ol, L["l2"],
+                         L["bias"], mi, ni)
+    nr = gu.nvfp4_nround(d.x_bf16.shape[1], L["rank"])
+    gu.assert_f32_within(y[mi, ni], ref, cond, nr)
+    yb = gu.host(gu.gemm(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], L["bias"],
+                         out_bf16=True, **kw))
+    gu.assert_bf16_close(yb[mi, ni], ref, cond, nr)
     ye = gu.host(gu.gemm(gc, gs, L["wcodes"], L["wscales"], gl, L["l2"], L["bias"], **kw))
     assert gu.rel_fro(ye[mi, ni], ref) <= 1e-3
 
@@ -139,9 +153,12 @@ def test_awq_modulation_gemv(workload_cache):
     e = gu.rel_fro(y, ref)
     print(f"awq rel_fro={e:.3e}")
     assert e <= 1e-3
+    cond = gu.awq_cond(A["x_prime"], A["qweight"], A["scales"], A["zeros"], A["bias"])
+    nr = gu.awq_nround(A["x_prime"].shape[1])
+    gu.assert_f32_within(y, ref, cond, nr)
     yb = gu.host(gu.awq(A["x_prime"], A["qweight"], A["scales"], A["zeros"], A["bias"],
                         out_bf16=True))
-    gu.assert_bf16_close(yb, ref)
+    gu.assert_bf16_close(yb, ref, cond, nr)
 
 
 def _quant_packed_exact(xb, L):
@@ -170,17 +187,20 @@ def test_attn_projection_packed(workload_cache):
     rng = np.random.default_rng(11)
     # GEMM stage on the oracle's activation-stage outputs
     ap = gu.pack_act(oc, os_, K)
+    mi, ni = _samples(rng, M, N)
+    ref = oracle.gemm_w4a4_int4_at(mi, ni, oc, os_, L["wcodes"], L["wscales"], ol, L["l2"],
+                                   L["bias"])
+    cond = gu.int4_cond(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], L["bias"], mi, ni)
+    nr = gu.int4_nround(K, L["rank"])
     for out_bf16 in (False, True):
         y = gu.host(gu.gemm_packed(ap, wp, M, K, N, ol, L["l2"], L["bias"], out_bf16=out_bf16))
-        mi, ni = _samples(rng, M, N)
-        ref = oracle.gemm_w4a4_int4_at(mi, ni, oc, os_, L["wcodes"], L["wscales"], ol, L["l2"],
-                                       L["bias"])
         if out_bf16:
-            gu.assert_bf16_close(y[mi, ni], ref)
+            gu.assert_bf16_close(y[mi, ni], ref, cond, nr)
         else:
             e = gu.rel_fro(y[mi, ni], ref)
             print(f"attn packed gemm rel_fro={e:.3e}")
             assert e <= 1e-3
+            gu.assert_f32_within(y[mi, ni], ref, cond, nr)
     # end to end: GPU chain vs oracle chain from the same X (fp32 output: bf16 rounding
     # alone is ~1e-3 relative and is checked element-wise above)
     ye = gu.host(gu.gemm_packed(buf, wp, M, K, N, gl, L["l2"], L["bias"]))
@@ -205,23 +225,28 @@ def test_mlp_pair_packed(workload_cache):
     mi1, ni1 = _samples(rng, M, N1, n_pts=2000)
     ref1 = oracle.gemm_w4a4_int4_at(mi1, ni1, oc1, os1, L1["wcodes"], L1["wscales"], ol1,
                                     L1["l2"], L1["bias"], act=1)
-    gu.assert_bf16_close(h_or[mi1, ni1], ref1)
-    # fc2 on its heavy-tailed calibration input: quantize-and-pack exact, GEMM sampled
+    cond1 = gu.int4_cond(oc1, os1, L1["wcodes"], L1["wscales"], ol1, L1["l2"], L1["bias"], mi1, ni1)
+    gu.assert_bf16_close(h_or[mi1, ni1], ref1, cond1, gu.int4_nround(K1, L1["rank"]), gelu=True)
+    # fc2 on its heavy-tailed calibration input: quantize-and-pack exact, GEMM sampled (fp32
+    # output with the workspace: the launch configuration the benchmark times, K split)
     x2 = d.extras["x2_bf16"]
     _, (oc3, os3, ol3) = _quant_packed_exact(x2, L2)
     wp2 = gu.prepack(L2["wcodes"], L2["wscales"], L2["wcodes"].shape[1] * 2, N2)
+    assert gu.split_workspace_bytes(x2.shape[0], x2.shape[1], N2) > 0
     y3 = gu.host(gu.gemm_packed(gu.pack_act(oc3, os3, x2.shape[1]), wp2, x2.shape[0],
-                                x2.shape[1], N2, ol3, L2["l2"], L2["bias"]))
+                                x2.shape[1], N2, ol3, L2["l2"], L2["bias"], split=True))
     mi3, ni3 = _samples(rng, *y3.shape, n_pts=2000)
     ref3 = oracle.gemm_w4a4_int4_at(mi3, ni3, oc3, os3, L2["wcodes"], L2["wscales"], ol3,
                                     L2["l2"], L2["bias"])
     e3 = gu.rel_fro(y3[mi3, ni3], ref3)
     print(f"mlp fc2 packed gemm rel_fro={e3:.3e}")
     assert e3 <= 1e-3
+    cond3 = gu.int4_cond(oc3, os3, L2["wcodes"], L2["wscales"], ol3, L2["l2"], L2["bias"], mi3, ni3)
+    gu.assert_f32_within(y3[mi3, ni3], ref3, cond3, gu.int4_nround(x2.shape[1], L2["rank"]))
     # GPU chain end to end on a few token rows against the oracle chain
     h = gu.gemm_packed(b1, wp1, M, K1, N1, gl1, L1["l2"], L1["bias"], act=1, out_bf16=True)
     b2, _, lo2 = gu.quantize_packed(h, L2["smooth_inv"], L2["l1"])
-    y = gu.host(gu.gemm_packed(b2, wp2, M, N1, N2, lo2, L2["l2"], L2["bias"]))
+    y = gu.host(gu.gemm_packed(b2, wp2, M, N1, N2, lo2, L2["l2"], L2["bias"], split=True))
     rows = np.array([0, 1, 777, 2048, 4095, M - 1])
     y1 = oracle.gemm_w4a4_int4(oc1[rows], os1[rows], L1["wcodes"], L1["wscales"], ol1[rows],
                                L1["l2"], L1["bias"], act=1)

@@ -99,8 +99,10 @@ def test_gemm_int4_shapes(M, N, K, r, bias, act):
     e = gu.rel_fro(y, ref)
     assert e <= 1e-3, e
     assert e <= 1e-5, f"fp32 output unexpectedly far from the oracle: {e}"
+    cond = gu.int4_cond(ca, sa, cw, sw, lora, l2, b)
+    gu.assert_f32_within(y, ref, cond, gu.int4_nround(K, r), gelu=act == 1)
     yb = gu.host(gu.gemm(ca, sa, cw, sw, lora, l2, b, act, out_bf16=True))
-    gu.assert_bf16_close(yb, ref)
+    gu.assert_bf16_close(yb, ref, cond, gu.int4_nround(K, r), gelu=act == 1)
 
 
 def test_gemm_int4_extreme_codes():

@@ -1,8 +1,9 @@
 """GPU parity of svdq_gemm_w4a4_packed_quantize_next, the MLP pair with fc2's activation
 kernel fused into fc1's GEMM epilogue: its packed codes, scale words and fp32 scales are
 bit-identical to fc1's packed GEMM (bf16 out) followed by svdq_quantize_act_packed, and
-its lora_act is within the fp32 summation bound of the oracle's down-projection of the
-same bf16 intermediate.  Shapes cover ragged token counts, fc1 widths that end in a
+its lora_act lies within the fp32 summation bound of the oracle's down-projection of the
+same bf16 intermediate (bit-equal to it wherever that bound reaches no bf16 rounding
+boundary), as the unfused activation kernel's does.  Shapes cover ragged token counts, fc1 widths that end in a
 partial 192-column tile, GELU on and off, next ranks 0 to 128, and the MLP end to end
 against the oracle chain."""
 import numpy as np
@@ -56,13 +57,13 @@ def test_fused_matches_unfused(M, K1, N1, r1, r2, act):
     if r2:
         hb = gu.host(h)
         ol = oracle.quant_act_int4(hb, si2, nl1)[2]
-        gu.assert_lora_close(gu.host(fl), ol, hb, nl1)
-        assert gu.bf16_ulp_diff(gu.host(fl), gu.host(ul)).max() <= 1
+        gu.assert_lora_close(gu.host(fl), ol, hb, nl1)     # fused: per-tile partials
+        gu.assert_lora_close(gu.host(ul), ol, hb, nl1)     # unfused: the activation kernel
 
 
 def test_fused_without_scales_and_repeat():
-    """next_act_scales NULL leaves the packed buffer unchanged, and a second call over the
-    same (dirty) workspace gives the same codes and lora_act."""
+    """next_act_scales NULL leaves the packed buffer unchanged, and a second call gives the
+    same codes and, bit for bit, the same lora_act (fixed-order sum of the tiles' partials)."""
     M, K1, N1, r1, r2 = 260, 192, 384, 16, 32
     rng = np.random.default_rng(1520)
     x, si1, l1, l2, cw, sw, b = _fc1(rng, M, K1, N1, r1)
@@ -75,7 +76,7 @@ def test_fused_without_scales_and_repeat():
                                                with_scales=False)
     torch.cuda.synchronize()
     assert s2 is None and torch.equal(b1, b2)
-    assert gu.bf16_ulp_diff(gu.host(l1o), gu.host(l2o)).max() <= 1
+    assert torch.equal(l1o, l2o), "lora_act differs between two calls"
 
 
 @pytest.mark.parametrize("M,K1,N1,N2,r", [(300, 256, 448, 200, 16), (700, 192, 768, 384, 32)])

@@ -50,8 +50,10 @@ def test_packed_gemm_shapes(M, N, K, r, bias, act):
     e = gu.rel_fro(y, ref)
     assert e <= 1e-3, e
     assert e <= 1e-4, f"unexpectedly far from the oracle: {e}"
+    cond = gu.int4_cond(ca, sa, cw, sw, lora, l2, b)
+    gu.assert_f32_within(y, ref, cond, gu.int4_nround(K, r), gelu=act == 1)
     yb = gu.host(gu.gemm_prepacked(ca, sa, packed, N, lora, l2, b, act, out_bf16=True))
-    gu.assert_bf16_close(yb, ref)
+    gu.assert_bf16_close(yb, ref, cond, gu.int4_nround(K, r), gelu=act == 1)
 
 
 def test_packed_gemm_unaligned_output_rows():
@@ -61,10 +63,12 @@ def test_packed_gemm_unaligned_output_rows():
     ca, sa, cw, sw, lora, l2, b = _inputs(rng, M, N, K, r)
     ref = oracle.gemm_w4a4_int4(ca, sa, cw, sw, lora, l2, b)
     packed = gu.prepack(cw, sw, K, N)
+    cond = gu.int4_cond(ca, sa, cw, sw, lora, l2, b)
     yb = gu.host(gu.gemm_prepacked(ca, sa, packed, N, lora, l2, b, out_bf16=True))
-    gu.assert_bf16_close(yb, ref)
+    gu.assert_bf16_close(yb, ref, cond, gu.int4_nround(K, r))
     y = gu.host(gu.gemm_prepacked(ca, sa, packed, N, lora, l2, b))
     assert gu.rel_fro(y, ref) <= 1e-4
+    gu.assert_f32_within(y, ref, cond, gu.int4_nround(K, r))
 
 
 def test_packed_extreme_codes():
@@ -94,24 +98,35 @@ def test_packed_matches_reference_kernel_and_is_deterministic():
 
 @pytest.mark.parametrize("M,N", [(4352, 3072), (4300, 2998)])
 def test_packed_gemm_k_split_last_round(M, N):
-    """17 x 16 output tiles on a 256-CU GPU: the last round's 16 tiles run as 8 K splits each,
-    added into the zeroed fp32 output.  The whole output against the nibble-operand kernel
-    (a different code path, itself checked against the oracle), samples against the oracle
-    (rows of the split tiles and of whole tiles); bf16 output (no split) at the samples."""
+    """17 x 16 output tiles on a 256-CU GPU: with a workspace, the last round's 16 tiles run
+    as 8 K splits each, summed in a fixed order by a second kernel.  The whole output against
+    the unsplit call (the same products in another fp32 order) and the nibble-operand kernel
+    (a different code path, itself checked against the oracle); samples against the oracle
+    within the fp32 error bound (rows of the split tiles and of whole tiles); two calls
+    bit-identical; bf16 output (no split) at the samples."""
     K, r = 1024, 32
     rng = np.random.default_rng(710 + M + N)
     ca, sa, cw, sw, lora, l2, b = _inputs(rng, M, N, K, r)
     print(f"packed gemm K split M={M} N={N} K={K} r={r}", flush=True)
+    assert gu.split_workspace_bytes(M, K, N) > 0, "this shape is expected to split"
     packed = gu.prepack(cw, sw, K, N)
-    y = gu.host(gu.gemm_prepacked(ca, sa, packed, N, lora, l2, b))
+    ap = gu.pack_act(ca, sa, K)
+    y = gu.host(gu.gemm_packed(ap, packed, M, K, N, lora, l2, b, split=True))
+    y_again = gu.host(gu.gemm_packed(ap, packed, M, K, N, lora, l2, b, split=True))
+    assert np.array_equal(y.view(np.uint32), y_again.view(np.uint32)), "K split not reproducible"
+    y1 = gu.host(gu.gemm_packed(ap, packed, M, K, N, lora, l2, b))
+    assert np.array_equal(y[:4096], y1[:4096]), "whole tiles differ between the two calls"
+    assert gu.rel_fro(y, y1) <= 1e-6
     y0 = gu.host(gu.gemm(ca, sa, cw, sw, lora, l2, b))
     assert gu.rel_fro(y, y0) <= 1e-5
     mi = np.concatenate([rng.integers(4096, M, 600), rng.integers(0, 4096, 200)])
     ni = rng.integers(0, N, mi.shape[0])
     ref = oracle.gemm_w4a4_int4_at(mi, ni, ca, sa, cw, sw, lora, l2, b)
     assert gu.rel_fro(y[mi, ni], ref) <= 1e-5
+    cond = gu.int4_cond(ca, sa, cw, sw, lora, l2, b, mi, ni)
+    gu.assert_f32_within(y[mi, ni], ref, cond, gu.int4_nround(K, r))
     yb = gu.host(gu.gemm_prepacked(ca, sa, packed, N, lora, l2, b, out_bf16=True))
-    gu.assert_bf16_close(yb[mi, ni], ref)
+    gu.assert_bf16_close(yb[mi, ni], ref, cond, gu.int4_nround(K, r))
 
 
 @pytest.mark.parametrize("M,K,r", [(1, 64, 0), (100, 192, 16), (256, 512, 32), (300, 1024, 32),
