@@ -24,6 +24,7 @@ __all__ = [
     "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
     "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
     "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy",
+    "svdq_gemm_w4a4_packed_noalloc",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -148,6 +149,13 @@ def svdq_gemm_w4a4_packed_ws(cfg, M, act_packed, prepacked, lora_act, l2, bias, 
         ctypes.byref(cfg), int(M), _ptr(act_packed), _ptr(prepacked), _ptr(lora_act), _ptr(l2),
         _ptr(bias), int(act), int(out_dtype), _ptr(out), _ptr(workspace), int(workspace_bytes),
         _stream(stream)))
+
+
+def svdq_gemm_w4a4_packed_noalloc(cfg, M, act_packed, prepacked, lora_act, l2, bias, act, out_dtype,
+                                  out, stream=None):
+    return _check(lib().svdq_gemm_w4a4_packed_noalloc(
+        ctypes.byref(cfg), int(M), _ptr(act_packed), _ptr(prepacked), _ptr(lora_act), _ptr(l2),
+        _ptr(bias), int(act), int(out_dtype), _ptr(out), _stream(stream)))
 
 
 def svdq_quantize_next_workspace_bytes(cfg, next_cfg, M):

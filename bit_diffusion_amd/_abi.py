@@ -30,7 +30,8 @@ EXPORTS = ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_
            "svdq_gemm_w4a4_packed_quantize_next", "svdq_calib_absmax", "svdq_smoothing_factors",
            "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
            "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
-           "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy")
+           "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy",
+           "svdq_gemm_w4a4_packed_noalloc")
 
 
 class LayerCfg(ctypes.Structure):
@@ -92,6 +93,7 @@ def lib():
         L.svdq_gemm_w4a4_packed_ws.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P, I64, P]
         L.svdq_quantize_next_workspace_bytes.argtypes = [cfgp, cfgp, I64,
                                                          ctypes.POINTER(ctypes.c_int64)]
+        L.svdq_gemm_w4a4_packed_noalloc.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P]
         L.svdq_peak_mfma.argtypes = [I32, I32, P, ctypes.POINTER(ctypes.c_int64), P]
         L.svdq_peak_copy.argtypes = [P, P, I64, P]
         L.svdq_check_device.argtypes = [ctypes.c_int]
@@ -109,7 +111,8 @@ def lib():
                      "svdq_calib_absmax", "svdq_smoothing_factors", "svdq_quantize_residual",
                      "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
                      "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
-                     "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy"):
+                     "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy",
+                     "svdq_gemm_w4a4_packed_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -26,7 +26,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["api.hip", "quant.hip", "gemm_int4.hip", "gemm_int4_fp6.hip", "gemm_nvfp4.hip",
-           "awq.hip", "lora.hip", "weights.hip", "lowrank.hip", "peaks.hip"]
+           "awq.hip", "lora.hip", "weights.hip", "lowrank.hip", "peaks.hip", "noalloc.hip"]
 # per-source extra flags: MFMA results in VGPRs (the fp32 rescale reads them with VALU ops)
 EXTRA = {"gemm_int4_fp6.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

@@ -421,6 +421,35 @@ svdq_status svdq_gemm_w4a4_packed_ws(const svdq_layer_cfg* cfg, int64_t M, const
                        workspace, workspace_bytes, stream, "svdq_gemm_w4a4_packed_ws");
 }
 
+svdq_status svdq_gemm_w4a4_packed_noalloc(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
+                                          const void* prepacked, const void* lora_act, const void* l2,
+                                          const void* bias, int32_t act, int32_t out_dtype, void* out,
+                                          svdq_stream_t stream) {
+    SVDQ_TRY(check_cfg(cfg));
+    SVDQ_TRY(check_int4(cfg));
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH)
+        return fail(SVDQ_ERR_INVALID_ARG, "act %d is not a svdq_act value", act);
+    if (out_dtype != SVDQ_DT_F32 && out_dtype != SVDQ_DT_BF16)
+        return fail(SVDQ_ERR_INVALID_ARG, "out_dtype %d is not a svdq_dtype value", out_dtype);
+    SVDQ_TRY(check_current_device());
+    void* ws = nullptr;
+    int64_t ws_bytes = 0;
+    const hipError_t e = svdq::noalloc_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess)
+        return fail(SVDQ_ERR_LAUNCH, "device scratch of svdq_gemm_w4a4_packed_noalloc not found: %s",
+                    hipGetErrorString(e));
+    const int64_t need = M == 0 ? 0
+                                : svdq::split_workspace_bytes(M, cfg->out_features, cfg->in_features, act,
+                                                              out_dtype == SVDQ_DT_BF16 ? 1 : 0);
+    if (need > ws_bytes)
+        return fail(SVDQ_ERR_UNSUPPORTED_CONFIG,
+                    "the K split needs %lld bytes of scratch, more than the %lld the library holds",
+                    (long long)need, (long long)ws_bytes);
+    return gemm_packed(cfg, M, act_packed, prepacked, lora_act, l2, bias, act, out_dtype, out, ws,
+                       need, stream, "svdq_gemm_w4a4_packed_noalloc");
+}
+
 svdq_status svdq_quantize_next_workspace_bytes(const svdq_layer_cfg* cfg, const svdq_layer_cfg* next_cfg,
                                                int64_t M, int64_t* bytes) {
     SVDQ_TRY(check_cfg(cfg));

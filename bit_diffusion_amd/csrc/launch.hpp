@@ -100,6 +100,8 @@ bool gemm_w4a4_fp6_init();
 void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st);
 int64_t split_workspace_bytes(int64_t M, int N, int K, int act_fn, int out_bf16);
 int cu_count();   // compute units of the current device (cached per device)
+// device address and size of the K-split scratch array of the current device (noalloc.hip)
+hipError_t noalloc_scratch(void** ptr, int64_t* bytes);
 
 // measurement kernels (peaks.hip)
 int64_t launch_mfma_peak(int kind, int iters, float* out, hipStream_t st);

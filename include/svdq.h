@@ -217,6 +217,23 @@ svdq_status svdq_gemm_w4a4_packed_ws(const svdq_layer_cfg* cfg, int64_t M, const
                                      const void* bias, int32_t act, int32_t out_dtype, void* out,
                                      void* workspace, int64_t workspace_bytes, svdq_stream_t stream);
 
+/* svdq_gemm_w4a4_packed_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as svdq_gemm_w4a4_packed_ws given svdq_gemm_w4a4_packed_workspace_bytes
+ * bytes of workspace (same split, same fixed-order sum, same bits), with the workspace taken
+ * from a 64 MiB device array inside the library instead of from the caller.  Each GPU the
+ * library runs on holds that array until the process ends; the call allocates nothing.
+ * All calls on one GPU share it and each call leaves its partial tiles in it: calls that
+ * may run at the same time on one GPU (different streams without ordering) race and must
+ * not be issued.  A split that would need more than the array holds is rejected with
+ * SVDQ_ERR_UNSUPPORTED_CONFIG (the split count is capped so that this does not happen on
+ * GPUs of up to 256 compute units).  Other arguments, results and errors as
+ * svdq_gemm_w4a4_packed. */
+svdq_status svdq_gemm_w4a4_packed_noalloc(const svdq_layer_cfg* cfg, int64_t M, const void* act_packed,
+                                          const void* prepacked, const void* lora_act, const void* l2,
+                                          const void* bias, int32_t act, int32_t out_dtype, void* out,
+                                          svdq_stream_t stream);
+
 /* Two chained linears on the packed path with the second one's activation kernel fused into
  * the first one's GEMM (the DiT MLP: fc1 with GELU, then fc2).  The pages credit the original
  * engine's extra speed to such per-architecture fusions of the GELU/MLP kernels (page
