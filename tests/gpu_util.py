@@ -308,6 +308,12 @@ def awq_nround(K):
     return 2 * (K + 2 * (K // 64) + 8)
 
 
+# The AWQ GEMV sums x (128 + q) and subtracts (128 + z) sum x per group: its fp32 partial
+# sums are ~16x the result's terms, so more of its bf16 outputs sit within the fp32 error
+# of a rounding boundary than the INT4 GEMMs' (measured 99.5-99.9 % bit-equal).
+AWQ_MIN_EXACT = 0.99
+
+
 def awq_cond(x_bf16, q, sc, z, bias=None):
     """Condition sum of each AWQ output [M, N]: sum_g s_g (sum_k |x_k| (128 + q_k) + (128 + z_g)
     sum_k |x_k|) + |b|, the magnitude bound of every partial sum of the bf16-MFMA form
