@@ -9,9 +9,10 @@ of 64, bf16 bias, bf16 output.
     python bench.py [--gpus 1] [--steps 50] [--warmup 40] [--no-cpu-baseline] [--only-main]
     python bench.py --copy-calibration      # plain 256 MiB device copies (counter calibration)
 
-The timed region is one replay of a HIP graph that holds exactly `--steps` steps (captured
-after the warmup, replayed once untimed, checked against an eager step); the same steps
-launched eagerly are reported as `ms_per_step_eager`.
+The timed region is one replay of a HIP graph that holds exactly `--steps` steps, right
+after `--warmup` steps of untimed replays (checked against an eager step); `--reps` more
+timed replays give the median, p10 and p90 per step, and the same steps launched eagerly
+are reported as `ms_per_step_eager`.
 
 Prints one JSON line.  `value` is TOPS of the linear, counting 2MNK + 2MNr + 2MKr
 operations per step (the low-rank branch's flops included, the dense bf16 work the method
@@ -67,7 +68,12 @@ def parse():
     ap.add_argument("--reps", type=int, default=100,
                     help="timed repetitions behind each median / p10 / p90")
     ap.add_argument("--leg", choices=["awq", "nvfp4", "mlp", "weights", "peaks"], default=None,
-                    help="run one secondary leg alone and print its JSON (profiling runs)")
+                    help="run one secondary leg alone and print its JSON")
+    ap.add_argument("--profile", choices=["quant", "gemm", "step", "mlp_fc1", "mlp_fc2",
+                                          "mlp_fused", "nvfp4", "awq", "peak_fp6", "peak_i8",
+                                          "copy"], default=None,
+                    help="eager launches of one kernel only (--steps of them after --warmup), "
+                         "no timing: the workload a profiler's counters are taken on")
     ap.add_argument("--only-main", action="store_true",
                     help="time only the W4A4 linear (no AWQ / NVFP4 legs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -159,7 +165,7 @@ def launch_stats(fn, batch, reps):
             "p90": round(float(np.percentile(t, 90)), 5), "reps": reps, "batch": batch}
 
 
-def awq_leg(reps, sp, stream):
+def awq_leg(reps, sp, stream, profile_calls=0):
     """AWQ W4A16 GEMV of the modulation layers: M=2, K=3072, N=18432, 14 rotating weight
     copies (> 400 MB, so every call streams its weights from HBM)."""
     import torch
@@ -187,6 +193,10 @@ def awq_leg(reps, sp, stream):
     for i in range(copies):
         go(i)
     torch.cuda.synchronize()
+    if profile_calls:
+        for i in range(profile_calls):
+            go(i)
+        return None
     st = launch_stats(go, 2 * copies, reps)
     ms = st["mean"]
     nbytes = Na * Ka // 2 + 2 * Na * (Ka // 64) * 2 + Ma * Ka * 2 + Na * 2 + Ma * Na * 4
@@ -197,7 +207,7 @@ def awq_leg(reps, sp, stream):
             "bytes": nbytes, "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def nvfp4_leg(reps, sp, stream):
+def nvfp4_leg(reps, sp, stream, profile_calls=0):
     """NVFP4 fused-QKV linear: activation kernel + GEMM, M=4096, K=3072, N=9216, rank 32."""
     import torch
     import synth
@@ -236,6 +246,10 @@ def nvfp4_leg(reps, sp, stream):
 
     go(0)
     torch.cuda.synchronize()
+    if profile_calls:
+        for i in range(profile_calls):
+            go(i)
+        return None
     stl = launch_stats(go, 5, reps)
     stg = launch_stats(gemm, 5, reps)
     ms, msg = stl["mean"], stg["mean"]
@@ -251,7 +265,11 @@ def nvfp4_leg(reps, sp, stream):
             "gemm_f16_peak_frac": round(tops_g / BF16_PEAK_TFLOPS, 4)}
 
 
-def mlp_leg(reps, sp, stream):
+def mlp_profile(what, calls, sp):
+    mlp_leg(0, sp, None, profile=(what, calls))
+
+
+def mlp_leg(reps, sp, stream, profile=None):
     """DiT MLP block on the packed path (M=4608 tokens, 3072 -> 12288 -> 3072, rank 32):
     fc1 with GELU(tanh) in its epilogue writing bf16, then fc2's activation kernel reads that
     output and fc2 writes fp32 (its nearly empty last round of tiles split over K in the
@@ -332,6 +350,12 @@ def mlp_leg(reps, sp, stream):
     go(0)
     go_fused(0)
     torch.cuda.synchronize()
+    if profile is not None:
+        what, calls = profile
+        fn = {"mlp_fc1": gemm1, "mlp_fc2": lambda i: gemm2(y, sp), "mlp_fused": fc1_fused}[what]
+        for i in range(calls):
+            fn(i)
+        return None
     # the two orders of the same block agree up to the fp32 order of fc2's down-projection
     fused_rel = float((yf - y).double().norm() / y.double().norm())
     if not fused_rel <= 1e-3:
@@ -578,11 +602,15 @@ def cpu_baseline(rows, threads, single_rows):
 
 def peaks_leg(sp, stream):
     """Measured denominators: each MFMA kind of the kernels at its sustained rate (a kernel
-    with independent back-to-back MFMAs on every SIMD, operands in registers), and a plain
-    copy through HBM (512 MiB each way, median of 20)."""
+    with independent back-to-back MFMAs on every SIMD, operands in registers); plain HBM
+    read and copy of 512 MiB (median of 20); and, in the launch mode the kernels are timed in
+    (graph replays of back-to-back launches over rotating buffers that defeat the last-level
+    cache), a plain read of the AWQ GEMV's bytes and a plain copy moving as many bytes as the
+    activation kernel."""
     import torch
     import bit_diffusion_amd as bd
-    out = torch.zeros(4, dtype=torch.float32, device="cuda:0")
+    dev = "cuda:0"
+    out = torch.zeros(4, dtype=torch.float32, device=dev)
     names = {0: "fp6_32x32x64", 1: "i8_32x32x32", 2: "bf16_32x32x16", 3: "bf16_32x32x8",
              4: "f16_32x32x16", 5: "fp4_32x32x64"}
     res = {}
@@ -599,21 +627,80 @@ def peaks_leg(sp, stream):
             torch.cuda.synchronize()
             best.append(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
         res[name] = round(float(np.median(best)), 1)
-    n = 512 << 20
-    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-    dst = torch.empty_like(src)
-    bd.svdq_peak_copy(src, dst, n, sp)
-    torch.cuda.synchronize()
-    gbs = []
-    for _ in range(20):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        bd.svdq_peak_copy(src, dst, n, sp)
-        e1.record(stream)
+
+    def big(fn, moved):
+        fn()
         torch.cuda.synchronize()
-        gbs.append(2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        r = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            r.append(moved / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        return round(float(np.median(r)), 1)
+
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_gbs = big(lambda: bd.svdq_peak_copy(src, dst, n, sp), 2 * n)
+    read_gbs = big(lambda: bd.svdq_peak_read(src, n, out, sp), n)
     del src, dst
-    return {"mfma_TOPS": res, "copy_GBs": round(float(np.median(gbs)), 1)}
+    # same size and launch mode as the AWQ GEMV (32,047,104 B read) and the activation
+    # kernel (25,165,824 B of x read; the copy moves 2 x 18.7 MB, its 37.4 MB)
+    na, nq, nb = 32047104, 37431296 // 2 // 16 * 16, 14
+    bufs = [torch.ones(max(na, nq), dtype=torch.uint8, device=dev) for _ in range(nb)]
+    outs = [torch.empty(nq, dtype=torch.uint8, device=dev) for _ in range(nb)]
+    st_r = launch_stats(lambda i, s_: bd.svdq_peak_read(bufs[i % nb], na, out, s_), 2 * nb, 100)
+    st_c = launch_stats(lambda i, s_: bd.svdq_peak_copy(bufs[i % nb], outs[i % nb], nq, s_), 2 * nb, 100)
+    del bufs, outs
+    return {"mfma_TOPS": res, "copy_GBs": copy_gbs, "read_GBs": read_gbs,
+            "read_awq_size_us": round(st_r["mean"] * 1e3, 3),
+            "read_awq_size_GBs": round(na / (st_r["mean"] * 1e-3) / 1e9, 1),
+            "copy_quant_size_us": round(st_c["mean"] * 1e3, 3),
+            "copy_quant_size_GBs": round(2 * nq / (st_c["mean"] * 1e-3) / 1e9, 1)}
+
+
+def profile_run(what, steps, warmup, sp):
+    """Eager launches of one kernel (warmup + steps of them) on the benchmark's inputs."""
+    import torch
+    import bit_diffusion_amd as bd
+    dev = "cuda:0"
+    if what in ("quant", "gemm", "step"):
+        si, sets, _ = make_inputs(4)
+        cfg = bd.LayerCfg.make(K, N, R)
+
+        def quant(s):
+            bd.svdq_quantize_act_packed(cfg, M, s["x"], si, s["l1p"], s["apacked"], s["scales"],
+                                        s["lora"], sp)
+
+        def gemm(s):
+            bd.svdq_gemm_w4a4_packed(cfg, M, s["apacked"], s["packed"], s["lora"], s["l2"],
+                                     s["bias"], bd.SVDQ_ACT_NONE, bd.SVDQ_DT_BF16, s["out"], sp)
+        for s in sets:
+            quant(s)
+        fn = {"quant": quant, "gemm": gemm, "step": lambda s: (quant(s), gemm(s))}[what]
+        for i in range(warmup + steps):
+            fn(sets[i % len(sets)])
+    elif what.startswith("mlp"):
+        mlp_profile(what, warmup + steps, sp)
+    elif what == "nvfp4":
+        nvfp4_leg(0, sp, None, profile_calls=warmup + steps)
+    elif what == "awq":
+        awq_leg(0, sp, None, profile_calls=warmup + steps)
+    elif what in ("peak_fp6", "peak_i8"):
+        out = torch.zeros(4, dtype=torch.float32, device=dev)
+        for _ in range(warmup + steps):
+            bd.svdq_peak_mfma(0 if what == "peak_fp6" else 1, 2048, out, sp)
+    else:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(warmup + steps):
+            bd.svdq_peak_copy(src, dst, n, sp)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": what, "launches": warmup + steps}), flush=True)
 
 
 def main():
@@ -631,7 +718,10 @@ def main():
     assert bd.svdq_check_device(0) == bd.SVDQ_OK, bd.svdq_last_error()
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    if args.leg is not None:   # one leg alone (for profiling runs)
+    if args.profile is not None:
+        profile_run(args.profile, args.steps, args.warmup, sp)
+        return
+    if args.leg is not None:   # one leg alone
         legs = {"awq": lambda: awq_leg(args.reps, sp, stream),
                 "nvfp4": lambda: nvfp4_leg(args.reps, sp, stream),
                 "mlp": lambda: mlp_leg(args.reps, sp, stream),
@@ -654,23 +744,16 @@ def main():
         quant(s, st)
         gemm(s, st)
 
-    for i in range(args.warmup):
+    for i in range(min(args.warmup, len(sets))):   # first touch of every input set
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # eager launches, for reference
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(sets[i % len(sets)])
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_eager = ev0.elapsed_time(ev1) / args.steps
-
     # whole-step timing: the `steps` steps captured once into a HIP graph (capturing runs
-    # nothing) and replayed, as a denoising loop launches its layers; one untimed replay
-    # first (the graph's first launch uploads it), then one timed replay: exactly `steps`
-    # steps between a synchronisation and an event pair on the replaying stream
+    # nothing) and replayed, as a denoising loop launches its layers.  The warmup is graph
+    # replays back to back (at least `warmup` steps; the first replay also uploads the
+    # graph), then one timed replay: exactly `steps` steps between a synchronisation and an
+    # event pair on the replaying stream
     cs = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(cs):
@@ -678,7 +761,8 @@ def main():
             for i in range(args.steps):
                 step(sets[i % len(sets)], cs.cuda_stream)
     torch.cuda.synchronize()
-    graph.replay()
+    for _ in range(max(1, -(-args.warmup // args.steps))):
+        graph.replay()
     torch.cuda.synchronize()
     ev0.record(stream)
     graph.replay()
@@ -693,6 +777,15 @@ def main():
     torch.cuda.synchronize()
     if not torch.equal(from_graph, sets[j]["out"]):
         raise RuntimeError("graph replay and eager launch disagree")
+
+    # eager launches of the same steps, for reference
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = ev0.elapsed_time(ev1) / args.steps
+
     # the spread: `reps` more timed replays of the same graph
     reps_t = []
     for _ in range(args.reps):
@@ -757,6 +850,7 @@ def main():
             "quantize_act_GBs": round(quant_gbs, 1),
             "quantize_act_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4),
             "quantize_act_copy_frac": round(quant_gbs / peaks["copy_GBs"], 4),
+            "quantize_act_frac_of_same_size_copy": round(quant_gbs / peaks["copy_quant_size_GBs"], 4),
             "gemm_ms": st_g["mean"],
             "gemm_TOPS": round(gemm_tops, 2),
         },
@@ -764,7 +858,8 @@ def main():
     }
     if not args.only_main:
         out["awq"] = awq_leg(args.reps, sp, stream)
-        out["awq"]["copy_frac"] = round(out["awq"]["GBs"] / peaks["copy_GBs"], 4)
+        out["awq"]["read_frac"] = round(out["awq"]["GBs"] / peaks["read_GBs"], 4)
+        out["awq"]["frac_of_same_size_read"] = round(out["awq"]["GBs"] / peaks["read_awq_size_GBs"], 4)
         out["nvfp4"] = nvfp4_leg(args.reps, sp, stream)
         out["mlp"] = mlp_leg(args.reps, sp, stream)
         out["lora"] = lora_leg(args.reps, sp, stream, si, sets)

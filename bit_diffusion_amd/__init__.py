@@ -24,7 +24,7 @@ __all__ = [
     "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
     "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
     "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy",
-    "svdq_gemm_w4a4_packed_noalloc",
+    "svdq_gemm_w4a4_packed_noalloc", "svdq_peak_read",
     "svdq_check_arch", "svdq_status_string", "svdq_last_error", "svdq_version", "LayerCfg",
     "SvdqError", "lib", "LIB_PATH",
 ]
@@ -214,6 +214,10 @@ def svdq_peak_mfma(kind, iters, out, stream=None):
 
 def svdq_peak_copy(src, dst, nbytes, stream=None):
     return _check(lib().svdq_peak_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)))
+
+
+def svdq_peak_read(src, nbytes, out, stream=None):
+    return _check(lib().svdq_peak_read(_ptr(src), int(nbytes), _ptr(out), _stream(stream)))
 
 
 def svdq_check_device(device=0):

@@ -31,7 +31,7 @@ EXPORTS = ("svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemm_w4a16", "svdq_check_
            "svdq_quantize_residual", "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
            "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
            "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy",
-           "svdq_gemm_w4a4_packed_noalloc")
+           "svdq_gemm_w4a4_packed_noalloc", "svdq_peak_read")
 
 
 class LayerCfg(ctypes.Structure):
@@ -96,6 +96,7 @@ def lib():
         L.svdq_gemm_w4a4_packed_noalloc.argtypes = [cfgp, I64, P, P, P, P, P, I32, I32, P, P]
         L.svdq_peak_mfma.argtypes = [I32, I32, P, ctypes.POINTER(ctypes.c_int64), P]
         L.svdq_peak_copy.argtypes = [P, P, I64, P]
+        L.svdq_peak_read.argtypes = [P, I64, P, P]
         L.svdq_check_device.argtypes = [ctypes.c_int]
         L.svdq_check_arch.argtypes = [ctypes.c_char_p]
         L.svdq_status_string.argtypes = [ctypes.c_int]
@@ -112,7 +113,7 @@ def lib():
                      "svdq_lowrank_workspace_bytes", "svdq_lowrank_factors",
                      "svdq_gemm_w4a4_packed_workspace_bytes", "svdq_gemm_w4a4_packed_ws",
                      "svdq_quantize_next_workspace_bytes", "svdq_peak_mfma", "svdq_peak_copy",
-                     "svdq_gemm_w4a4_packed_noalloc"):
+                     "svdq_gemm_w4a4_packed_noalloc", "svdq_peak_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -621,6 +621,16 @@ svdq_status svdq_peak_copy(const void* src, void* dst, int64_t bytes, svdq_strea
     return after_launch("svdq_peak_copy");
 }
 
+svdq_status svdq_peak_read(const void* src, int64_t bytes, void* out, svdq_stream_t stream) {
+    if (bytes <= 0 || bytes % 16 != 0)
+        return fail(SVDQ_ERR_INVALID_ARG, "bytes = %lld must be a positive multiple of 16", (long long)bytes);
+    SVDQ_TRY(check_ptr(src, "src", 16));
+    SVDQ_TRY(check_ptr(out, "out", 4));
+    SVDQ_TRY(check_current_device());
+    svdq::launch_read(src, bytes, out, reinterpret_cast<hipStream_t>(stream));
+    return after_launch("svdq_peak_read");
+}
+
 svdq_status svdq_check_device(int device) { return check_device_ordinal(device); }
 
 svdq_status svdq_check_arch(const char* arch_name) {
@@ -631,7 +641,11 @@ svdq_status svdq_check_arch(const char* arch_name) {
 }
 
 const char* svdq_status_string(svdq_status status) {
-    switch (status) {
+    // the caller may pass any 32-bit value: read it as an integer, not as the enum (a value
+    // outside the enum's range may not be loaded as the enum type)
+    int32_t s;
+    std::memcpy(&s, &status, sizeof s);
+    switch (s) {
         case SVDQ_OK: return "SVDQ_OK";
         case SVDQ_ERR_INVALID_ARG: return "SVDQ_ERR_INVALID_ARG: invalid argument";
         case SVDQ_ERR_UNSUPPORTED_DEVICE: return "SVDQ_ERR_UNSUPPORTED_DEVICE: device is not gfx950";

@@ -106,6 +106,7 @@ hipError_t noalloc_scratch(void** ptr, int64_t* bytes);
 // measurement kernels (peaks.hip)
 int64_t launch_mfma_peak(int kind, int iters, float* out, hipStream_t st);
 void launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+void launch_read(const void* src, int64_t bytes, void* out, hipStream_t st);
 int64_t quantize_next_workspace_bytes(int64_t M, int N, int next_r);
 
 // offline weight quantization (weights.hip)

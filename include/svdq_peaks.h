@@ -18,7 +18,11 @@
  * svdq_peak_copy: dst[0, bytes) = src[0, bytes), 16-byte loads and stores, a grid-stride
  *   loop over the whole GPU; src and dst device memory, 16-byte aligned, not overlapping,
  *   bytes a positive multiple of 16.  It moves 2 * bytes through HBM.
- * Both check the device like every other entry point and enqueue on `stream`.
+ * svdq_peak_read: loads src[0, bytes) once (16-byte non-temporal loads, a grid-stride loop
+ *   with four loads per thread in flight); `out` is device memory of at least 4 bytes,
+ *   written only with a value the data cannot produce (so in practice never).  bytes a
+ *   positive multiple of 16, src 16-byte aligned.  It moves `bytes` through HBM.
+ * All check the device like every other entry point and enqueue on `stream`.
  */
 #ifndef SVDQ_PEAKS_H
 #define SVDQ_PEAKS_H
@@ -34,6 +38,7 @@ extern "C" {
 svdq_status svdq_peak_mfma(int32_t kind, int32_t iters, float* out, int64_t* ops,
                            svdq_stream_t stream);
 svdq_status svdq_peak_copy(const void* src, void* dst, int64_t bytes, svdq_stream_t stream);
+svdq_status svdq_peak_read(const void* src, int64_t bytes, void* out, svdq_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -204,3 +204,38 @@ def test_quantize_packed_then_gemm_end_to_end():
     buf, _, lora = gu.quantize_packed(x, si, l1)
     y = gu.host(gu.gemm_packed(buf, gu.prepack(cw, sw, K, N), M, K, N, lora, l2, b))
     assert gu.rel_fro(y, ref) <= 1e-3
+
+
+def test_tiny_workload_packed_end_to_end():
+    """The tiny workload (256 tokens, K = N = 512, rank 16, no bias) through the calls the
+    benchmark times: svdq_prepack_l1 + svdq_quantize_act_packed (codes read back from the
+    packed buffer and fp32 scales bit-exact, lora_act within its fp32 bound), then
+    svdq_prepack_weight + svdq_gemm_w4a4_packed (fp32 output within the fp32 error bound of
+    the oracle element by element and 1e-3 relative Frobenius; bf16 output among the bf16
+    roundings of that bound)."""
+    from oracle.construct import build_workload
+    d, (L,) = build_workload(synth.WORKLOADS[0])
+    M, K = d.x_bf16.shape
+    N, r = L["wcodes"].shape[0], L["rank"]
+    print(f"tiny workload packed M={M} K={K} N={N} r={r}", flush=True)
+    buf, scales, lora = gu.quantize_packed(d.x_bf16, L["smooth_inv"], L["l1"], N=N)
+    torch.cuda.synchronize()
+    oc, os_, ol = oracle.quant_act_int4(d.x_bf16, L["smooth_inv"], L["l1"])
+    q, words, canonical = gu.decode_act_packed(gu.host(buf), M, K)
+    assert canonical
+    assert np.array_equal(q[:M], oracle.unpack_int4(oc).astype(np.int64)), "codes differ"
+    assert np.array_equal(gu.host(scales).view(np.uint32), os_.view(np.uint32)), "scales differ"
+    gu.assert_lora_close(gu.host(lora), ol, d.x_bf16, L["l1"])
+    wp = gu.prepack(L["wcodes"], L["wscales"], K, N)
+    ref = oracle.gemm_w4a4_int4(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], None)
+    cond = gu.int4_cond(oc, os_, L["wcodes"], L["wscales"], ol, L["l2"], None)
+    # GEMM on the oracle's activation outputs: element-wise bound
+    y = gu.host(gu.gemm_packed(gu.pack_act(oc, os_, K), wp, M, K, N, ol, L["l2"], None))
+    gu.assert_f32_within(y, ref, cond, gu.int4_nround(K, r))
+    yb = gu.host(gu.gemm_packed(gu.pack_act(oc, os_, K), wp, M, K, N, ol, L["l2"], None, out_bf16=True))
+    gu.assert_bf16_close(yb, ref, cond, gu.int4_nround(K, r))
+    # end to end from the GPU's own activation stage
+    ye = gu.host(gu.gemm_packed(buf, wp, M, K, N, lora, L["l2"], None))
+    assert gu.rel_fro(ye, ref) <= 1e-3
+    exact = oracle.bf16_to_f64(d.x_bf16) @ d.w.T   # and the method did its job
+    assert gu.rel_fro(ye, exact) < 0.2
