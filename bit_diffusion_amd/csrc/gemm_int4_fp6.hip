@@ -17,12 +17,13 @@
 // pipeline stage is a plain copy: 26 KiB per (256x192 tile, group) moved global -> LDS by
 // the LDS-DMA path (global_load_lds_dwordx4).  LDS holds a ring of three buffers of two
 // groups; while one buffer computes, the next one's copies land and the copies of the one
-// after are issued, spread over the computation.
+// after are issued in its first two steps (the barrier that opens a buffer also releases
+// the one read before it, which these copies overwrite).
 //
 // The two groups of a buffer run as one software pipeline of twelve 32x32 sub-tiles: the
 // two MFMAs of sub-tile q+1 are issued around the fmas of sub-tile q, across the group
 // boundary too, and the second group's operands are read from LDS while the first group's
-// last column computes.  Copy source addresses are kept in SGPRs.
+// last two columns compute.  Copy source addresses are kept in SGPRs.
 //
 // Tiling: 256x192 output tile per 512-thread workgroup, 8 waves as 4 x 2, each 64x96 =
 // 2 x 3 tiles of 32x32 (two waves per SIMD, whose MFMA and VALU work overlap).  Workgroup
@@ -60,6 +61,9 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));
 }
+
+// s_waitcnt lgkmcnt(0) alone: every earlier LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Workgroup barrier without the memory fence __syncthreads() adds (that fence would wait
 // for all in-flight DMA); LDS ordering comes from wait_vm before it.
@@ -134,6 +138,9 @@ __device__ __forceinline__ void work_of(const PackedGemmArgs& p, int num_m, int 
     }
     tile_of(t, pid_m, pid_n, num_m, num_n);
 }
+
+// What the bias loads read when there is no bias.
+__device__ const uint16_t kZeroBf16[1] = {0};
 
 // Epilogue staging: each wave writes its 32 x 96 half-tiles to LDS and stores whole
 // 16-byte row segments.  Row strides are chosen so that the two 4-row halves of a
@@ -214,13 +221,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
 #pragma unroll
             for (int j = 0; j < 3; ++j) lb[j][c] = *reinterpret_cast<const uint4*>(l2 + (int64_t)ncol[j] * r + 16 * c + 8 * fh);
         }
-    const uint16_t* bias = (const uint16_t*)p.bias;
-    float bv[3];
+    // The bias as raw bf16, loaded without a branch (a load under a divergent branch gets
+    // a wait for every load in flight right after it); with no bias, or in a K split other
+    // than the first, the loads read a zero instead.  Converted in the epilogue.
+    const bool has_bias = p.bias != nullptr && split <= 0;
+    const uint16_t* bsrc = has_bias ? (const uint16_t*)p.bias : kZeroBf16;
+    uint32_t braw[3];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int col = n0 + wn * 96 + j * 32 + fr;
-        bv[j] = (bias && col < N && split <= 0) ? bf16_to_f32(bias[col]) : 0.0f;
-    }
+    for (int j = 0; j < 3; ++j) braw[j] = bsrc[has_bias ? ncol[j] : 0];
 
     // Buffer (third) t holds groups 2t and 2t + 1, 52 chunks: chunk c is chunk c % 26 of
     // group 2t + c / 26.  Wave w copies chunks w + 8 j, j = 0..6 (j = 6 exists for w < 4
@@ -262,7 +270,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         for (int j = 0; j < 3; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    wait_vm<0>();   // the first half and the operands above have landed
+    // the operands above and the first two groups have landed (with four groups issued,
+    // at most the 6 or 8 copies of groups 2 and 3 are in flight)
+    if (G >= 4) wait_vm<6>();
+    else wait_vm<0>();
 #pragma unroll
     for (int c = 0; c < 2; ++c)
         if (16 * c < r) {
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     // operands, three weight fragments and theirs.
     struct Frags {
         i32x8 a[2];
-        bf16x4 ap[2];
+        uint2 ax[2];   // the activation scale words, made into the MFMA operand by ap_of
         i32x8 w[3];
         bf16x4 wp[3];
     };
@@ -302,12 +313,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
             // with its neighbour it would need two moves)
             const uint64_t v1q = *(const volatile __attribute__((address_space(3))) uint64_t*)(Ab + 1024 + lane * 8);
             const uint2 v1 = make_uint2((uint32_t)v1q, (uint32_t)(v1q >> 32));
-            const uint2 x = *reinterpret_cast<const uint2*>(Ab + kFrag + fr * 8);
+            f.ax[i] = *reinterpret_cast<const uint2*>(Ab + kFrag + fr * 8);
             f.a[i].s0123 = i32x4{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w};
             f.a[i].s45 = (__attribute__((ext_vector_type(2))) int){(int)v1.x, (int)v1.y};
-            // (h | m << 16, l) -> lanes 0-31 (h, h, m, h), lanes 32-63 (l, m, m, l)
-            f.ap[i] = __builtin_bit_cast(bf16x4, make_uint2(__builtin_amdgcn_perm(x.x, x.y, psel0),
-                                                            __builtin_amdgcn_perm(x.x, x.y, psel1)));
         }
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -320,11 +328,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
             f.wp[j] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(Bb + kFrag + lane * 8));
         }
     };
+    // The activation scale operand of the scale-product MFMA from the row's two words
+    // (h | m << 16, l): lanes 0-31 (h, h, m, h), lanes 32-63 (l, m, m, l).  Formed right
+    // before its MFMA, so the LDS read behind it has had time to land.
+    auto ap_of = [&](uint2 x) {
+        return __builtin_bit_cast(bf16x4, make_uint2(__builtin_amdgcn_perm(x.x, x.y, psel0),
+                                                     __builtin_amdgcn_perm(x.x, x.y, psel1)));
+    };
     // Software-pipelined: the two MFMAs of pair q+1 are issued around the fmas of pair q,
     // so the MFMA pipe and the VALU work at the same time within one wave.
     auto compute = [&](const Frags& f) {
         f32x16 r0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[0], f.w[0], f32x16{}, 2, 2, 0, 127, 0, 127);
-        f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(f.ap[0], f.wp[0], f32x16{}, 0, 0, 0);
+        f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ap_of(f.ax[0]), f.wp[0], f32x16{}, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < 6; ++q) {
             const int i = q & 1, j = q >> 1;
@@ -339,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
             __builtin_amdgcn_sched_barrier(0);
             if (q < 5) {
                 const int i1 = (q + 1) & 1, j1 = (q + 1) >> 1;
-                p1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(f.ap[i1], f.wp[j1], f32x16{}, 0, 0, 0);
+                p1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ap_of(f.ax[i1]), f.wp[j1], f32x16{}, 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -352,11 +367,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
 
     // Both groups of a third in one software pipeline of twelve 32x32 sub-tiles (no drain
     // and refill between the groups): the second group's operands are read once the first
-    // group's first two columns are issued, `between` runs after the first group's FMAs
-    // have started the second group's MFMAs.
+    // group is done with its weight columns 0 and 1; `between(q)` runs after steps 0 and 1.
     auto compute2 = [&](const Frags& fa, Frags& fb, const uint8_t* Sb, auto&& between) {
         f32x16 r0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa.a[0], fa.w[0], f32x16{}, 2, 2, 0, 127, 0, 127);
-        f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fa.ap[0], fa.wp[0], f32x16{}, 0, 0, 0);
+        f32x16 p0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ap_of(fa.ax[0]), fa.wp[0], f32x16{}, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < 12; ++q) {
             const int i = q & 1, j = (q >> 1) % 3;
@@ -369,17 +383,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[i][j][e] = fmaf(r0[e], p0[e], acc[i][j][e]);
             __builtin_amdgcn_sched_barrier(0);
-            if (q < 11) p1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fn.ap[i1], fn.wp[j1], f32x16{}, 0, 0, 0);
+            if (q < 11) p1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ap_of(fn.ax[i1]), fn.wp[j1], f32x16{}, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 8; e < 16; ++e) acc[i][j][e] = fmaf(r0[e], p0[e], acc[i][j][e]);
             __builtin_amdgcn_sched_barrier(0);
-            if (q == 3) {   // the first group's weight columns 0 and 1 are no longer read
+            if (q == 2) {   // sub-tile 3's MFMAs are issued: the first group's weight
+                            // columns 0 and 1 are no longer read
+                // The first group's reads have landed by now; waiting for them here keeps
+                // the LDS counter (at most 15 in flight) from forcing a wait on the oldest
+                // of the 15 reads below instead.
+                wait_lgkm0();
                 load_frags(Sb, fb);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (q == 5) {
-                between();
+            if (q <= 1) {
+                between(q);
                 __builtin_amdgcn_sched_barrier(0);
             }
             r0 = r1;
@@ -395,14 +414,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         {
             Frags f, f1;
             load_frags(S, f);
-            compute2(f, f1, S + kStageBytes, [&] {
+            // third t+2's copies go into third t-1's buffer, which the barrier above
+            // released, early in the third so they have two thirds to land
+            compute2(f, f1, S + kStageBytes, [&](int q) {
+                if (q == 0) {
 #pragma unroll
-                for (int j = 0; j < 3; ++j) issue_j(t + 2, j);   // third t+2's copies, spread over the third
+                    for (int j = 0; j < 3; ++j) issue_j(t + 2, j);
+                } else {
+#pragma unroll
+                    for (int j = 3; j < 7; ++j) issue_j(t + 2, j);
+                }
             });
             __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int j = 3; j < 7; ++j) issue_j(t + 2, j);
     }
     // tail: thirds t and t+1 are issued; at most one group (2t+4 = G-1) is not
     wait_vm<0>();
@@ -430,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         for (int j = 0; j < 3; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                float v = acc[i][j][e] + bv[j];
+                float v = acc[i][j][e] + __uint_as_float(braw[j] << 16);
                 if constexpr (kGelu) v = gelu_tanh(v);
                 acc[i][j][e] = v;
             }
