@@ -6,7 +6,7 @@ GEMM (per-group dequantization, low-rank up-projection, bias), for the DiT atten
 projection at 1024x1024 image scale: M = 4096 tokens, K = N = 3072, rank 32, INT4 groups
 of 64, bf16 bias, bf16 output.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 40] [--no-cpu-baseline] [--only-main]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 500] [--no-cpu-baseline] [--only-main]
     python bench.py --copy-calibration      # plain 256 MiB device copies (counter calibration)
 
 The timed region is one replay of a HIP graph that holds exactly `--steps` steps, right
@@ -53,8 +53,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=40,
-                    help="untimed steps first (the clocks settle over the first few ms of load)")
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first (the clocks settle over the first tens of ms of load)")
     ap.add_argument("--copies", type=int, default=10,
                     help="rotating input sets (each ~30 MB) to defeat the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -69,7 +69,7 @@ def parse():
                     help="timed repetitions behind each median / p10 / p90")
     ap.add_argument("--leg", choices=["awq", "nvfp4", "mlp", "weights", "peaks"], default=None,
                     help="run one secondary leg alone and print its JSON")
-    ap.add_argument("--profile", choices=["quant", "gemm", "step", "mlp_fc1", "mlp_fc2",
+    ap.add_argument("--profile", choices=["quant", "gemm", "step", "mlp_fc1", "mlp_fc2", "mlp_q2",
                                           "mlp_fused", "nvfp4", "awq", "peak_fp6", "peak_i8",
                                           "copy"], default=None,
                     help="eager launches of one kernel only (--steps of them after --warmup), "
@@ -352,7 +352,8 @@ def mlp_leg(reps, sp, stream, profile=None):
     torch.cuda.synchronize()
     if profile is not None:
         what, calls = profile
-        fn = {"mlp_fc1": gemm1, "mlp_fc2": lambda i: gemm2(y, sp), "mlp_fused": fc1_fused}[what]
+        fn = {"mlp_fc1": gemm1, "mlp_fc2": lambda i: gemm2(y, sp), "mlp_fused": fc1_fused,
+              "mlp_q2": lambda i: quant(fc2, h, sp)}[what]
         for i in range(calls):
             fn(i)
         return None
