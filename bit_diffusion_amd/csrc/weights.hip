@@ -99,8 +99,10 @@ __global__ __launch_bounds__(256) void smooth_factor_kernel(const float* __restr
 // (binary64), the smoothed weight is w_hat = w lam_k; the low-rank branch carries
 // (l2 l1)[n, k] lam_k (l1 absorbs smooth_inv, so un-smoothing it gives the branch's share of
 // w_hat); the residual is R = fp32(w_hat - (l2 l1) lam).  (l2 l1)[n, k] sums r products of
-// two bf16 values: each product is exact in binary64 and so is their sum (while the r
-// products span fewer than 2^37 in magnitude), so no summation order changes it.  Thread t:
+// two bf16 values.  Each product is exact in binary64: a 16-bit integer times 2^e_j.  Their
+// sum, and every partial sum, is then an integer multiple of 2^(min e_j) below
+// r 2^16 2^(max e_j), exact in binary64's 53 bits while max e_j - min e_j <= 37 - ceil(log2 r)
+// (32 at rank 32, 30 at rank 128); within that no summation order changes it.  Thread t:
 // row t / (K / 32), channels 32 (t % (K / 32)) .. + 31; the lanes t, t ^ 1 share a 64-group.
 struct ResidualArgs {
     const float* w;

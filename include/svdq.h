@@ -120,6 +120,11 @@ svdq_status svdq_quantize_act(const svdq_layer_cfg* cfg, int64_t M, const void* 
  *              INT4:  y = sum_g sa[m,g] sw[n,g] sum_{k in g} qa[m,k] qw[n,k]
  *              NVFP4: y = S_a S_w sum_k e_a[m,k] sb_a[m,k/16] e_w[n,k] sb_w[n,k/16]
  *              plus sum_j lora_act[m,j] l2[n,j] + bias[n], accumulated in fp32.
+ * For INT4 this call is the reference path on the plain nibble format: it contracts the
+ * nibbles on the int8 MFMA with 128x128 tiles (about 151 us at M = 4096, K = N = 3072 on
+ * an MI355X).  The primary INT4 path is the packed one below (svdq_prepack_weight once per
+ * layer, svdq_quantize_act_packed, svdq_gemm_w4a4_packed: about 46 us for that GEMM), with
+ * the same result up to fp32 rounding order.
  */
 svdq_status svdq_gemm_w4a4(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
                            const void* act_scales, float act_global_scale,
@@ -292,8 +297,9 @@ svdq_status svdq_gemm_w4a4_packed_quantize_next(
  *   per-tensor scale S_w = fp32(max |R| / 2688) is written to wgt_global_scale (one fp32
  *   in device memory, the GEMM's weight_global_scale), then wgt_codes [N, K/2] E2M1 and
  *   wgt_scales [N, K/16] E4M3 bytes under it.  The low-rank product sums bf16 products in
- *   binary64, exact while each element's products span less than 2^37, so the codes and
- *   scales are those of the definition bit for bit.
+ *   binary64.  Each product is a 16-bit integer times 2^e_j, so the sum is exact while an
+ *   element's exponents satisfy max e_j - min e_j <= 37 - ceil(log2 r) (32 at rank 32);
+ *   the codes and scales are then those of the definition bit for bit.
  * svdq_lowrank_factors: the branch's factors between the two, from the leading r singular
  *   triplets of the smoothed weight W diag(lambda) (lambda = 1 / smooth_inv), split as
  *   sqrt(sigma) on each side: l2 bf16 [N, r] = U sqrt(sigma), l1 bf16 [r, K] =
