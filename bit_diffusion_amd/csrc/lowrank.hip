@@ -125,8 +125,9 @@ __device__ void sum_gram(const double* part, int nblk, int b, double (*G)[kW + 1
 #pragma unroll
             for (int i = 0; i < kW; ++i) acc[i] += pk[i * kW];
         }
+    if (t < kW)
 #pragma unroll
-    for (int i = 0; i < kW; ++i) G[i][t] = i < b ? acc[i] : 0.0;
+        for (int i = 0; i < kW; ++i) G[i][t] = i < b ? acc[i] : 0.0;
     __syncthreads();
 }
 
@@ -184,10 +185,12 @@ __global__ __launch_bounds__(256) void apply_rinv_kernel(float* __restrict__ X, 
     if (r < rows) X[r * kW + j] = s;
 }
 
-// Z^T Z = U_B diag(sigma^2) U_B^T by cyclic Jacobi (one wave, binary64), eigenvalues sorted
-// in decreasing order: ub[i][j] (64 x 64, the first r columns used), sigma[j] = sqrt(ev_j).
-__global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ part, int nblk, int b,
-                                                    float* __restrict__ ub, float* __restrict__ sigma) {
+// Z^T Z = U_B diag(sigma^2) U_B^T by cyclic Jacobi (binary64, kJacobiThreads threads: the
+// rotations of a round are applied by all of them), eigenvalues sorted in decreasing order:
+// ub[i][j] (64 x 64, the first r columns used), sigma[j] = sqrt(ev_j).
+constexpr int kJacobiThreads = 256;
+__global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __restrict__ part, int nblk, int b,
+                                                                float* __restrict__ ub, float* __restrict__ sigma) {
     __shared__ double S[kW][kW + 1];   // padded: column walks stay conflict-free
     __shared__ double V[kW][kW + 1];   // padded: column walks stay conflict-free
     __shared__ int order[kW];
@@ -195,7 +198,8 @@ __global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ p
     __shared__ double pc[kW / 2], ps[kW / 2];
     const int t = threadIdx.x;
     sum_gram(part, nblk, b, S);
-    for (int i = 0; i < kW; ++i) V[i][t] = i == t ? 1.0 : 0.0;
+    if (t < kW)
+        for (int i = 0; i < kW; ++i) V[i][t] = i == t ? 1.0 : 0.0;
     __syncthreads();
     // Parallel cyclic Jacobi, round-robin ordering: with nb = b rounded up to even, a sweep
     // is nb - 1 rounds; round r pairs the positions i and nb - 1 - i of the list
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ p
                 pp[t] = p, pq[t] = q, pc[t] = c, ps[t] = sn;
             }
             __syncthreads();
-            for (int it = t; it < np * b; it += kW) {   // columns p, q of S and V
+            for (int it = t; it < np * b; it += kJacobiThreads) {   // columns p, q of S and V
                 const int pr = it / b, k = it - pr * b;
                 const double sn = ps[pr];
                 if (sn == 0.0) continue;
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ p
                 V[k][q] = sn * vp + c * vq;
             }
             __syncthreads();
-            for (int it = t; it < np * b; it += kW) {   // rows p, q of S
+            for (int it = t; it < np * b; it += kJacobiThreads) {   // rows p, q of S
                 const int pr = it / b, k = it - pr * b;
                 const double sn = ps[pr];
                 if (sn == 0.0) continue;
@@ -268,7 +272,8 @@ __global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ p
         }
     }
     __syncthreads();
-    for (int i = 0; i < kW; ++i) ub[i * kW + t] = t < b && i < b ? (float)V[i][order[t]] : 0.0f;
+    if (t < kW)
+        for (int i = 0; i < kW; ++i) ub[i * kW + t] = t < b && i < b ? (float)V[i][order[t]] : 0.0f;
     if (t < b) sigma[t] = (float)__builtin_sqrt(fmax(S[order[t]][order[t]], 0.0));
 }
 
@@ -385,14 +390,15 @@ void launch_lowrank_factors(int N, int K, int r, int b, int iters, const float* 
     }
     skinny<true>(w, smooth_inv, N, K, wk.Q, wk.Z, wk, st);
     hipLaunchKernelGGL(gram_partial_kernel, gK, dim3(256), 0, st, (const float*)wk.Z, K, wk.part);
-    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(64), 0, st, (const double*)wk.part, (int)gK.x, b, wk.ub,
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kJacobiThreads), 0, st, (const double*)wk.part, (int)gK.x, b, wk.ub,
                        wk.sigma);
     const int64_t tot = (int64_t)N * r + (int64_t)r * K;
     hipLaunchKernelGGL(factors_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
                        (const float*)wk.Q, (const float*)wk.Z, (const float*)wk.ub, (const float*)wk.sigma,
                        smooth_inv, N, K, r, b, (uint16_t*)l1, (uint16_t*)l2);
-    if (sigma_out)
-        hipMemcpyAsync(sigma_out, wk.sigma, (size_t)r * 4, hipMemcpyDeviceToDevice, st);
+    // a failed copy leaves its error as the thread's last HIP error, which the API call
+    // reports right after this launcher returns
+    if (sigma_out) (void)hipMemcpyAsync(sigma_out, wk.sigma, (size_t)r * 4, hipMemcpyDeviceToDevice, st);
 }
 
 }  // namespace svdq

@@ -91,3 +91,21 @@ def test_lowrank_gaussian_captured_energy(N, K, r):
     eg, eo = _captured(w_hat, l1, l2, lam), _captured(w_hat, o1, o2, lam)
     print(f"gauss {N}x{K} captured energy ratio {eg / eo:.4f}")
     assert eg <= eo * (1 + 1e-3) and eg >= 0.95 * eo
+
+
+def test_lowrank_attention_weight_captured_energy():
+    # the attention projection's own smoothed weight (3072 x 3072, calibration from its
+    # 4096-token draw with 31 outlier channels x50) at the benchmark's settings (block 48,
+    # four iterations): its 31 outlier directions stand well above the bulk, so the branch
+    # captures all but a sliver of what the exact top-32 branch does
+    wl = synth.WORKLOADS[1]
+    d = synth.draw(wl)
+    w64 = d.w.astype(np.float32).astype(np.float64)
+    si, lam = smoothing(d.x_bf16, w64)
+    rng = np.random.default_rng(1730)
+    l1, l2, sig = _factor(w64.astype(np.float32), si, 32, 48, 4, rng)
+    o1, o2, _, _ = lowrank_residual(w64, si, lam, 32)
+    w_hat = w64 * lam[None, :]
+    eg, eo = _captured(w_hat, l1, l2, lam), _captured(w_hat, o1, o2, lam)
+    print(f"attention weight captured energy ratio {eg / eo:.6f}")
+    assert eg <= eo * (1 + 1e-4) and eg >= 0.999 * eo
