@@ -52,6 +52,7 @@ static_assert(kAChunks + kBChunks == 26, "chunk assignment below assumes 26 chun
 constexpr int kSmemBytes = kStages * kStageBytes;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt with vmcnt = n (lgkmcnt = 0): every earlier LDS access of this wave has
@@ -633,8 +634,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
                 const uint4 v = *reinterpret_cast<const uint4*>(stg + lr * kStride + ls * 16);
                 const int64_t row = m0 + wm * 64 + i * 32 + lr;
                 const int col = n0 + wn * 96 + ls * (16 / kEsz);
+                // streaming stores: the output is written once and read by the next
+                // layer's kernel, so it need not allocate in the L2 on its way out
                 if (row < M && col < N)
-                    *reinterpret_cast<uint4*>((uint8_t*)p.out + (row * N + col) * kEsz) = v;
+                    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                                reinterpret_cast<u32x4*>((uint8_t*)p.out + (row * N + col) * kEsz));
             }
         }
     } else {

@@ -220,6 +220,48 @@ __device__ __forceinline__ f16x2 scale_pair(uint32_t sc, int byte) {
     return f16x2{v, v};
 }
 
+// The output tile through LDS: each wave writes its 32 x 96 half-tiles to its own region
+// and stores whole 16-byte row segments, non-temporal (the output is written once and read
+// by the next layer's kernel).  Row strides keep the two 4-row halves of a 32x32 MFMA
+// output on disjoint banks.  A wave's LDS accesses complete in order, so the reads see the
+// writes before them and the next half's writes land after them.  N * esz must be a
+// multiple of 16 and the output 16-byte aligned.
+typedef unsigned nv_u32x4 __attribute__((ext_vector_type(4)));
+template <bool kBf16>
+__device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[2][3], uint8_t* smem, const GemmArgs& p,
+                                                  int64_t m0, int n0, int wave, int wm, int wn, int lane) {
+    constexpr int kEsz = kBf16 ? 2 : 4;
+    constexpr int kStride = kBf16 ? 208 : 416;
+    constexpr int kSegs = 96 * kEsz / 16;   // 16-byte segments per 96-column row
+    static_assert((32 * kSegs) % 64 == 0, "whole segments per lane");
+    const int fr = lane & 31, fh = lane >> 5;
+    const int64_t M = p.M;
+    const int N = p.N;
+    uint8_t* stg = smem + wave * (32 * kStride);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                uint8_t* dst = stg + (8 * (e >> 2) + 4 * fh + (e & 3)) * kStride + (j * 32 + fr) * kEsz;
+                if constexpr (kBf16) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f32_to_bf16(acc[i][j][e]);
+                else *reinterpret_cast<float*>(dst) = acc[i][j][e];
+            }
+#pragma unroll
+        for (int t = 0; t < 32 * kSegs / 64; ++t) {
+            const int c = lane + 64 * t;
+            const int lr = c / kSegs, ls = c % kSegs;
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + lr * kStride + ls * 16);
+            const int64_t row = m0 + wm * 64 + i * 32 + lr;
+            const int col = n0 + wn * 96 + ls * (16 / kEsz);
+            if (row < M && col < N)
+                __builtin_nontemporal_store(nv_u32x4{v.x, v.y, v.z, v.w},
+                                            reinterpret_cast<nv_u32x4*>((uint8_t*)p.out + (row * N + col) * kEsz));
+        }
+    }
+}
+
 __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p) {
     extern __shared__ __align__(16) uint8_t fsm[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -365,18 +407,35 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int col = n0 + wn * 96 + j * 32 + fr;
-        const bool cok = col < N;
-        const float bv = (bias && cok) ? bf16_to_f32(bias[col]) : 0.0f;
+        const float bv = (bias && col < N) ? bf16_to_f32(bias[col]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float v = acc[i][j][e] + bv;
+                if (p.act == 1) v = gelu_tanh(v);
+                acc[i][j][e] = v;
+            }
+    }
+    const int esz = p.out_bf16 ? 2 : 4;
+    if (((int64_t)N * esz) % 16 == 0 && (reinterpret_cast<uintptr_t>(p.out) % 16) == 0) {
+        fbarrier();   // every wave is done with the stage buffers
+        if (p.out_bf16) store_tile_staged<true>(acc, fsm, p, m0, n0, wave, wm, wn, lane);
+        else store_tile_staged<false>(acc, fsm, p, m0, n0, wave, wm, wn, lane);
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int col = n0 + wn * 96 + j * 32 + fr;
+        if (col >= N) continue;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-                float v = acc[i][j][e] + bv;
-                if (p.act == 1) v = gelu_tanh(v);
-                if (cok && row < M) {
-                    if (p.out_bf16) ((uint16_t*)p.out)[row * N + col] = (uint16_t)f32_to_bf16(v);
-                    else ((float*)p.out)[row * N + col] = v;
+                if (row < M) {
+                    if (p.out_bf16) ((uint16_t*)p.out)[row * N + col] = (uint16_t)f32_to_bf16(acc[i][j][e]);
+                    else ((float*)p.out)[row * N + col] = acc[i][j][e];
                 }
             }
     }
