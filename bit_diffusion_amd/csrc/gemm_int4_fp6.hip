@@ -774,23 +774,41 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict
 }
 
 // The next layer's lora_act from the fused epilogue's per-tile partial sums: lora[m, j] =
-// bf16(sum over column tiles t = 0, 1, ... of ws[t][m][j]) in that order, rounded once to
-// nearest even.  One thread per four consecutive ranks of a row.
+// bf16(sum over the column tiles t of ws[t][m][j]), rounded once to nearest even, in a fixed
+// order: the tiles are cut into kLoraChunks consecutive runs, each run summed in order by
+// its own thread, then the run sums added in order.  A block holds 32 items (a row's four
+// consecutive ranks) x kLoraChunks runs.
+constexpr int kLoraChunks = 8;
 __global__ __launch_bounds__(256) void sum_lora_kernel(const float* __restrict__ ws,
                                                        uint16_t* __restrict__ lora, int64_t M,
                                                        int64_t Mpad, int R2, int ntn) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (m, 4 ranks)
+    __shared__ f32x4 part[kLoraChunks][32];
+    const int it = threadIdx.x & 31, c = threadIdx.x >> 5;
+    const int64_t idx = (int64_t)blockIdx.x * 32 + it;   // (m, 4 ranks)
     const int q = R2 / 4;
-    if (idx >= M * q) return;
-    const int64_t m = idx / q;
-    const int j = 4 * (int)(idx % q);
+    const bool ok = idx < M * q;
+    const int64_t m = ok ? idx / q : 0;
+    const int j = ok ? 4 * (int)(idx % q) : 0;
+    const int run = (ntn + kLoraChunks - 1) / kLoraChunks;
+    const int t0 = c * run, t1 = min(ntn, t0 + run);
     const float* src = ws + m * R2 + j;
     const int64_t stride = Mpad * R2;
-    f32x4 v = *reinterpret_cast<const f32x4*>(src);
-    for (int t = 1; t < ntn; ++t) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(src + t * stride);
-        v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (ok && t0 < t1) {
+        v = *reinterpret_cast<const f32x4*>(src + t0 * stride);
+        for (int t = t0 + 1; t < t1; ++t) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(src + t * stride);
+            v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+        }
     }
+    part[c][it] = v;
+    __syncthreads();
+    if (c != 0 || !ok) return;
+    for (int k = 1; k < kLoraChunks; ++k)
+        if (k * run < ntn) {
+            const f32x4 w = part[k][it];
+            v = f32x4{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+        }
     const uint32_t lo = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
     const uint32_t hi = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
     *reinterpret_cast<uint2*>(lora + m * R2 + j) = make_uint2(lo, hi);
@@ -871,7 +889,7 @@ void launch_gemm_w4a4_fp6(const PackedGemmArgs& a, hipStream_t st) {
         else hipLaunchKernelGGL((gemm_w4a4_fp6_kernel<true, false, true>), grid, block, kSmemBytes, st, b);
         if (a.next_r > 0) {
             const int64_t n = a.M * (a.next_r / 4);
-            hipLaunchKernelGGL(sum_lora_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+            hipLaunchKernelGGL(sum_lora_kernel, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, st,
                                (const float*)a.lora_work, (uint16_t*)a.out, a.M, (int64_t)num_m * kBM,
                                a.next_r, num_n);
         }

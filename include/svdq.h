@@ -256,8 +256,10 @@ svdq_status svdq_gemm_w4a4_packed_noalloc(const svdq_layer_cfg* cfg, int64_t M, 
  * scale words and next_act_scales are bit-identical to the unfused pair; next_lora_act
  * (bf16 [M, next rank]) is the same sum in another fp32 order: each 192-column tile stores
  * its fp32 partial sums in lora_workspace and a second kernel adds the tiles' partials in
- * column order and rounds once, so it is bit-reproducible (and within one bf16 ulp of the
- * unfused pair where the two fp32 sums straddle a rounding boundary).
+ * a fixed order (eight consecutive runs of tiles, each summed in column order, then the
+ * runs in order) and rounds once, so it is bit-reproducible; like the unfused pair's, each
+ * element lies within the fp32 error bound of the exact sum (the two differ only where
+ * that bound straddles a bf16 rounding boundary).
  * next_cfg->in_features must equal cfg->out_features (both INT4).  next_l1 is the next
  * layer's row-major bf16 [rank, K] factor (not prepacked); lora_workspace is caller-owned
  * device scratch of svdq_quantize_next_workspace_bytes(cfg, next_cfg, M) bytes
