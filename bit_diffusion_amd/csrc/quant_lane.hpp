@@ -98,22 +98,22 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
     return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// Nearest E2M1 magnitude (0, .5, 1, 1.5, 2, 3, 4, 6), ties to the even code, saturating;
-// sign in bit 3.
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-    float a = fabsf(v);
-    uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-               : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
-    return c | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 // NVFP4 for the lane's 32 values: two blocks of 16 (channels 0-15 are ev/od 0-7), each with
 // the E4M3 scale sb = e4m3(absmax / (6 S)) and E2M1 codes of v / (e4m3_decode(sb) S) (all
 // zero where sb is 0).  d: the 16 code bytes, low nibble the even channel; sbs: the two
 // scale bytes (block 0 in the low byte).
+//
+// The quotient is the correctly rounded fp32 v / dq without a division per value: with
+// r = 1 / dq correctly rounded, q0 = v r lies within one ulp of v / dq, so the remainder
+// v - q0 dq is exact (one fma) and q0 + remainder * r rounds to v / dq (Markstein's
+// theorem on division by a correctly rounded reciprocal).  That needs no overflow and no
+// underflow of the remainder: blocks with dq below 2^-100 or quotients that could reach
+// 2^100 take the plain division instead.  A quotient that underflows has code 0 whichever
+// way it rounds.  The sign of the code is v's (also for v = -0).  The E2M1 rounding is
+// v_cvt_scalef32_pk_fp4_f32's with scale 1: nearest, ties to the even code, saturating
+// at 6; the first source goes to the low nibble.
 __device__ __forceinline__ void nvfp4_codes32(const Vals& v, float S, uint32_t (&d)[4], uint32_t& sbs) {
     const float den = 6.0f * S;
-    d[0] = d[1] = d[2] = d[3] = 0u;
     sbs = 0u;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -122,14 +122,38 @@ __device__ __forceinline__ void nvfp4_codes32(const Vals& v, float S, uint32_t (
         for (int i = 8 * b; i < 8 * b + 8; ++i) a = fmaxf(a, fmaxf(fabsf(v.ev[i]), fabsf(v.od[i])));
         const uint32_t sb = e4m3_encode(a / den);
         sbs |= sb << (8 * b);
-        if (sb != 0u) {
-            const float dq = e4m3_decode(sb) * S;
+        const float dq = e4m3_decode(sb) * S;
+        const float r = 1.0f / dq;
+        float qe[8], qo[8];
+        if (sb == 0u || (dq >= 0x1p-100f && a * r < 0x1p100f)) {
 #pragma unroll
-            for (int i = 8 * b; i < 8 * b + 8; ++i) {
-                const uint32_t pair = e2m1_encode(v.ev[i] / dq) | (e2m1_encode(v.od[i] / dq) << 4);
-                d[i >> 2] |= pair << (8 * (i & 3));
+            for (int i = 0; i < 8; ++i) {
+                const float e0 = v.ev[8 * b + i] * r, o0 = v.od[8 * b + i] * r;
+                qe[i] = __builtin_fmaf(__builtin_fmaf(-e0, dq, v.ev[8 * b + i]), r, e0);
+                qo[i] = __builtin_fmaf(__builtin_fmaf(-o0, dq, v.od[8 * b + i]), r, o0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qe[i] = v.ev[8 * b + i] / dq;
+                qo[i] = v.od[8 * b + i] / dq;
             }
         }
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float e = __builtin_copysignf(qe[i], v.ev[8 * b + i]);
+            const float o = __builtin_copysignf(qo[i], v.od[8 * b + i]);
+            uint32_t& wk = w[i >> 2];
+            switch (i & 3) {   // the byte selector must be a constant
+                case 0: wk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wk, e, o, 1.0f, 0); break;
+                case 1: wk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wk, e, o, 1.0f, 1); break;
+                case 2: wk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wk, e, o, 1.0f, 2); break;
+                default: wk = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wk, e, o, 1.0f, 3); break;
+            }
+        }
+        d[2 * b] = sb ? w[0] : 0u;
+        d[2 * b + 1] = sb ? w[1] : 0u;
     }
 }
 

@@ -39,6 +39,54 @@ def test_quant_nvfp4_shapes(M, K, r):
             gu.assert_lora_close(gu.host(lora), ol, xb, l1)
 
 
+E2M1_TIES = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+
+
+def test_quant_nvfp4_ties_saturation_and_tiny_scales():
+    """Quotients exactly on the E2M1 rounding ties, one bf16 step on either side of them,
+    above 6 (saturation), -0 and an all-zero block.  S = fp32(1/6) makes every block
+    divisor exactly 1 (block amax 6, or 6.25 whose E4M3 scale rounds to 6), so the
+    quotients are the values themselves; the same rows scaled by 2^-112 with S scaled
+    alike give divisors below 2^-100, where the kernel divides plainly.  Codes and scales
+    bit-exact, and the oracle's codes at the ties are the even neighbours."""
+    rng = np.random.default_rng(471)
+    ties = np.array(list(E2M1_TIES), np.float32)
+    up = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(ties) + 1)
+    dn = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(ties) - 1)
+    rows = []
+    for m in range(24):
+        sg = lambda n: rng.choice([-1.0, 1.0], n).astype(np.float32)
+        b0 = np.concatenate([[6.0], ties * sg(7), ties[:4] * sg(4), [0.0, -0.0, 2.0 ** -10, -(2.0 ** -10)]])
+        b1 = np.concatenate([[6.25], up * sg(7), dn * sg(7), [-6.125]])
+        b2 = np.zeros(16, np.float32)
+        b2[rng.integers(0, 16, 5)] = -0.0
+        b3 = np.concatenate([[-6.0], [6.0, 5.5, -4.5, 3.25, 2.75, 2.25, 1.5], ties[-4:] * sg(4),
+                             [0.5, -0.0, 0.125, -0.375]])
+        blocks = [rng.permutation(b).astype(np.float32) for b in (b0, b1, b2, b3)]
+        rows.append(np.concatenate(blocks))
+    x = np.stack(rows).astype(np.float32)
+    xb = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(synth.bf16_bits_to_f32(xb), x)   # every value is a bf16 value
+    K = x.shape[1]
+    si = np.ones(K, np.float32)
+    S = np.float32(1.0) / np.float32(6.0)
+    # the oracle's codes at the exact ties (blocks 0 and 3, divisor 1) are the even ones
+    oc, os_, _ = oracle.quant_act_nvfp4(xb, si, S, None)
+    vals = oracle.unpack_u4(oc).astype(np.int64)
+    mag = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])[vals & 7]
+    for t, want in E2M1_TIES.items():
+        sel = np.abs(x) == np.float32(t)
+        sel[:, 16:32] = False   # block 1's divisor differs only by its own scale, checked below
+        assert np.all(mag[sel] == want), t
+    assert np.all(mag[:, 16:32][np.abs(x[:, 16:32]) > 6.0] == 6.0)   # saturation
+    for xx, SS in ((x, S), (x * np.float32(2.0 ** -112), np.float32(S * np.float32(2.0 ** -112)))):
+        xxb = synth.f32_to_bf16_bits(xx)
+        codes, scales, _ = gu.quantize(xxb, si, None, "nvfp4", float(SS))
+        oc, os_, _ = oracle.quant_act_nvfp4(xxb, si, SS, None)
+        assert np.array_equal(gu.host(scales), os_)
+        assert np.array_equal(gu.host(codes), oc)
+
+
 # K a multiple of 256 takes the fast kernel (two, three and four 256-channel stages over
 # several 256 x 192 tiles with ragged row and column tails); other K the reference kernel.
 @pytest.mark.parametrize("M,N,K,r,bias,act", [
