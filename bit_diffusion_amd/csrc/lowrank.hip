@@ -90,26 +90,48 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict
     out[t] = s;
 }
 
-// part[blk] = X[64 blk .. + 63, :]^T X[...] in binary64 (rows past `rows` are zero)
+// part[blk] = X[kGramRows blk .. + kGramRows - 1, :]^T X[...] in binary64 (rows past `rows`
+// are zero).  Thread tid owns the entries tid + 256 e, e = 0..15, and runs their sums side by
+// side over the rows in order (each product of two fp32 values is exact in binary64).
+constexpr int kGramRows = 16;
 __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restrict__ X, int rows,
                                                            double* __restrict__ part) {
-    __shared__ float xs[kW][kW];
+    __shared__ float xs[kGramRows][kW];
     const int tid = threadIdx.x;
-    const int r0 = blockIdx.x * kW;
+    const int r0 = blockIdx.x * kGramRows;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < kGramRows * kW / 256; ++e) {
         const int idx = tid + 256 * e, rr = idx >> 6, cc = idx & 63;
         xs[rr][cc] = r0 + rr < rows ? X[(int64_t)(r0 + rr) * kW + cc] : 0.0f;
     }
     __syncthreads();
+    double s[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.0;
+    const int j = tid & 63;
+    for (int r = 0; r < kGramRows; ++r) {
+        const double xj = xs[r][j];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] += (double)xs[r][(tid >> 6) + 4 * e] * xj;
+    }
     double* out = part + (int64_t)blockIdx.x * kW * kW;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int idx = tid + 256 * e, i = idx >> 6, j = idx & 63;
-        double s = 0.0;
-        for (int r = 0; r < kW; ++r) s += (double)xs[r][i] * (double)xs[r][j];
-        out[idx] = s;
-    }
+    for (int e = 0; e < 16; ++e) out[tid + 256 * e] = s[e];
+}
+
+// gsum[e] = sum of the partial Gram matrices part[k][e], so that the single-wave kernels
+// below read one 64 x 64 matrix.  A block takes 64 entries; its four waves sum consecutive
+// quarters of k in order, and the quarter sums are added in order (a fixed order).
+__global__ __launch_bounds__(256) void gram_sum_kernel(const double* __restrict__ part, int nblk,
+                                                       double* __restrict__ gsum) {
+    __shared__ double qs[4][64];
+    const int q = threadIdx.x >> 6, e = blockIdx.x * 64 + (threadIdx.x & 63);   // grid: kW * kW / 64
+    const int len = (nblk + 3) / 4, k0 = q * len, k1 = min(nblk, k0 + len);
+    double s = 0.0;
+    for (int k = k0; k < k1; ++k) s += part[(int64_t)k * kW * kW + e];
+    qs[q][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (q == 0) gsum[e] = ((qs[0][threadIdx.x] + qs[1][threadIdx.x]) + qs[2][threadIdx.x]) + qs[3][threadIdx.x];
 }
 
 // Sum the partial Gram matrices into LDS (b x b used), one wave: lane t keeps column t of
@@ -207,11 +229,25 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __
     // pairs of a round are disjoint.  Each round takes every pair's rotation from S as the
     // round finds it, then applies all of them: columns (S and V), then rows.
     const int nb = (b + 1) & ~1, np = nb / 2;
+    __shared__ double red[2][kJacobiThreads];
+    __shared__ int stop;
     for (int sweep = 0; sweep < 30; ++sweep) {
+        // off-diagonal and diagonal squares: each thread sums a fixed set of entries, thread
+        // 0 adds the per-thread sums in thread order
         double off = 0.0, dia = 0.0;
-        for (int i = 0; i < b; ++i)
-            for (int j = 0; j < b; ++j) (i == j ? dia : off) += S[i][j] * S[i][j];
-        if (off <= 1e-24 * dia) break;   // every lane sees the same S
+        for (int e = t; e < b * b; e += kJacobiThreads) {
+            const int i = e / b, j = e - i * b;
+            (i == j ? dia : off) += S[i][j] * S[i][j];
+        }
+        red[0][t] = off, red[1][t] = dia;
+        __syncthreads();
+        if (t == 0) {
+            double o = 0.0, d = 0.0;
+            for (int k = 0; k < kJacobiThreads; ++k) o += red[0][k], d += red[1][k];
+            stop = o <= 1e-24 * d;
+        }
+        __syncthreads();
+        if (stop) break;
         for (int rd = 0; rd < nb - 1; ++rd) {
             if (t < np) {
                 const int i0 = t, i1 = nb - 1 - t;
@@ -234,29 +270,44 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __
                 pp[t] = p, pq[t] = q, pc[t] = c, ps[t] = sn;
             }
             __syncthreads();
-            for (int it = t; it < np * b; it += kJacobiThreads) {   // columns p, q of S and V
-                const int pr = it / b, k = it - pr * b;
-                const double sn = ps[pr];
-                if (sn == 0.0) continue;
-                const int p = pp[pr], q = pq[pr];
-                const double c = pc[pr];
-                const double kp = S[k][p], kq = S[k][q];
-                S[k][p] = c * kp - sn * kq;
-                S[k][q] = sn * kp + c * kq;
-                const double vp = V[k][p], vq = V[k][q];
-                V[k][p] = c * vp - sn * vq;
-                V[k][q] = sn * vp + c * vq;
-            }
-            __syncthreads();
-            for (int it = t; it < np * b; it += kJacobiThreads) {   // rows p, q of S
-                const int pr = it / b, k = it - pr * b;
-                const double sn = ps[pr];
-                if (sn == 0.0) continue;
-                const int p = pp[pr], q = pq[pr];
-                const double c = pc[pr];
-                const double pk = S[p][k], qk = S[q][k];
-                S[p][k] = c * pk - sn * qk;
-                S[q][k] = sn * pk + c * qk;
+            // S <- J^T S J and V <- V J in one pass.  J rotates each pair (p, q) of the round:
+            // column p <- c col p - s col q, column q <- s col p + c col q, and rows alike.
+            // The pairs cover every index, so S splits into 2 x 2 blocks (rows of pair a,
+            // columns of pair e), each updated from its own old values: columns first, then
+            // rows -- the same operations, in the same order, as rotating all columns and
+            // then all rows.
+            for (int it = t; it < 32 * 32 + 32 * kW; it += kJacobiThreads) {
+                if (it < 32 * 32) {
+                    const int a = it >> 5, e = it & 31;
+                    if (a >= np || e >= np) continue;
+                    const double sa = ps[a], se = ps[e];
+                    if (sa == 0.0 && se == 0.0) continue;
+                    const int pa = pp[a], qa = pq[a], pe = pp[e], qe = pq[e];
+                    double m00 = S[pa][pe], m01 = S[pa][qe], m10 = S[qa][pe], m11 = S[qa][qe];
+                    if (se != 0.0) {
+                        const double ce = pc[e];
+                        const double n00 = ce * m00 - se * m01, n01 = se * m00 + ce * m01;
+                        const double n10 = ce * m10 - se * m11, n11 = se * m10 + ce * m11;
+                        m00 = n00, m01 = n01, m10 = n10, m11 = n11;
+                    }
+                    if (sa != 0.0) {
+                        const double ca = pc[a];
+                        const double n00 = ca * m00 - sa * m10, n10 = sa * m00 + ca * m10;
+                        const double n01 = ca * m01 - sa * m11, n11 = sa * m01 + ca * m11;
+                        m00 = n00, m01 = n01, m10 = n10, m11 = n11;
+                    }
+                    S[pa][pe] = m00, S[pa][qe] = m01, S[qa][pe] = m10, S[qa][qe] = m11;
+                } else {
+                    const int u = it - 32 * 32, pr = u >> 6, k = u & 63;
+                    if (pr >= np || k >= b) continue;
+                    const double sn = ps[pr];
+                    if (sn == 0.0) continue;
+                    const int p = pp[pr], q = pq[pr];
+                    const double c = pc[pr];
+                    const double vp = V[k][p], vq = V[k][q];
+                    V[k][p] = c * vp - sn * vq;
+                    V[k][q] = sn * vp + c * vq;
+                }
             }
             __syncthreads();
         }
@@ -314,19 +365,21 @@ __global__ __launch_bounds__(256) void pad_kernel(const float* __restrict__ src,
     dst[t] = j < b ? src[r * b + j] : 0.0f;
 }
 
-constexpr int kSlices = 5;   // inner-dimension slices of a skinny product
+constexpr int kSlices = 20;  // inner-dimension slices of a skinny product (enough blocks to fill the GPU)
 
 struct Work {
     float *Q, *Z, *rinv, *ub, *sigma, *slices;
-    double* part;
+    double *part, *gsum;
 };
 
 Work carve(void* ws, int N, int K) {
-    const int nblk = (std::max(N, K) + kW - 1) / kW;
+    const int nblk = (std::max(N, K) + kGramRows - 1) / kGramRows;
     uint8_t* p = (uint8_t*)ws;
     Work w;
     w.part = (double*)p;
     p += (int64_t)nblk * kW * kW * 8;
+    w.gsum = (double*)p;
+    p += (int64_t)kW * kW * 8;
     w.slices = (float*)p;
     p += (int64_t)kSlices * std::max(N, K) * kW * 4;
     w.Q = (float*)p;
@@ -356,10 +409,12 @@ void skinny(const float* W, const float* smooth_inv, int N, int K, const float* 
 }
 
 void orth(float* X, int rows, int b, const Work& w, hipStream_t st) {
-    const int nblk = (rows + kW - 1) / kW;
+    const int nblk = (rows + kGramRows - 1) / kGramRows;
     for (int pass = 0; pass < 2; ++pass) {   // CholeskyQR2
         hipLaunchKernelGGL(gram_partial_kernel, dim3(nblk), dim3(256), 0, st, (const float*)X, rows, w.part);
-        hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(64), 0, st, (const double*)w.part, nblk, b, w.rinv);
+        hipLaunchKernelGGL(gram_sum_kernel, dim3(kW * kW / 64), dim3(256), 0, st, (const double*)w.part, nblk,
+                           w.gsum);
+        hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(64), 0, st, (const double*)w.gsum, 1, b, w.rinv);
         hipLaunchKernelGGL(apply_rinv_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, X, rows,
                            (const float*)w.rinv);
     }
@@ -368,8 +423,8 @@ void orth(float* X, int rows, int b, const Work& w, hipStream_t st) {
 }  // namespace
 
 int64_t lowrank_workspace_bytes(int N, int K) {
-    const int nblk = (std::max(N, K) + kW - 1) / kW;
-    return (int64_t)nblk * kW * kW * 8 + (int64_t)kSlices * std::max(N, K) * kW * 4 +
+    const int nblk = (std::max(N, K) + kGramRows - 1) / kGramRows;
+    return (int64_t)(nblk + 1) * kW * kW * 8 + (int64_t)kSlices * std::max(N, K) * kW * 4 +
            (int64_t)(N + K) * kW * 4 + 2 * kW * kW * 4 + kW * 4;
 }
 
@@ -377,7 +432,7 @@ void launch_lowrank_factors(int N, int K, int r, int b, int iters, const float* 
                             const float* smooth_inv, const float* omega, void* l1, void* l2,
                             float* sigma_out, void* workspace, hipStream_t st) {
     const Work wk = carve(workspace, N, K);
-    const dim3 gK((unsigned)((K + kW - 1) / kW));
+    const dim3 gK((unsigned)((K + kGramRows - 1) / kGramRows));
     hipLaunchKernelGGL(pad_kernel, dim3((unsigned)(((int64_t)K * kW + 255) / 256)), dim3(256), 0, st, omega, K,
                        b, wk.Z);
     skinny<false>(w, smooth_inv, N, K, wk.Z, wk.Q, wk, st);
@@ -390,7 +445,9 @@ void launch_lowrank_factors(int N, int K, int r, int b, int iters, const float* 
     }
     skinny<true>(w, smooth_inv, N, K, wk.Q, wk.Z, wk, st);
     hipLaunchKernelGGL(gram_partial_kernel, gK, dim3(256), 0, st, (const float*)wk.Z, K, wk.part);
-    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kJacobiThreads), 0, st, (const double*)wk.part, (int)gK.x, b, wk.ub,
+    hipLaunchKernelGGL(gram_sum_kernel, dim3(kW * kW / 64), dim3(256), 0, st, (const double*)wk.part, (int)gK.x,
+                       wk.gsum);
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kJacobiThreads), 0, st, (const double*)wk.gsum, 1, b, wk.ub,
                        wk.sigma);
     const int64_t tot = (int64_t)N * r + (int64_t)r * K;
     hipLaunchKernelGGL(factors_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
