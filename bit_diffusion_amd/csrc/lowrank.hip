@@ -134,6 +134,16 @@ __global__ __launch_bounds__(256) void gram_sum_kernel(const double* __restrict_
     if (q == 0) gsum[e] = ((qs[0][threadIdx.x] + qs[1][threadIdx.x]) + qs[2][threadIdx.x]) + qs[3][threadIdx.x];
 }
 
+// A summed Gram matrix (64 x 64, b x b used) into LDS, zero outside b x b: threads t < 64
+// copy column t.
+__device__ void load_gram(const double* g, int b, double (*G)[kW + 1]) {
+    const int t = threadIdx.x;
+    if (t < kW)
+#pragma unroll 8
+        for (int i = 0; i < kW; ++i) G[i][t] = i < b && t < b ? g[i * kW + t] : 0.0;
+    __syncthreads();
+}
+
 // Sum the partial Gram matrices into LDS (b x b used), one wave: lane t keeps column t of
 // all 64 rows in registers, so each partial's 64 loads are independent.
 __device__ void sum_gram(const double* part, int nblk, int b, double (*G)[kW + 1]) {
@@ -210,8 +220,8 @@ __global__ __launch_bounds__(256) void apply_rinv_kernel(float* __restrict__ X, 
 // Z^T Z = U_B diag(sigma^2) U_B^T by cyclic Jacobi (binary64, kJacobiThreads threads: the
 // rotations of a round are applied by all of them), eigenvalues sorted in decreasing order:
 // ub[i][j] (64 x 64, the first r columns used), sigma[j] = sqrt(ev_j).
-constexpr int kJacobiThreads = 256;
-__global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __restrict__ part, int nblk, int b,
+constexpr int kJacobiThreads = 1024;
+__global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __restrict__ gram, int b,
                                                                 float* __restrict__ ub, float* __restrict__ sigma) {
     __shared__ double S[kW][kW + 1];   // padded: column walks stay conflict-free
     __shared__ double V[kW][kW + 1];   // padded: column walks stay conflict-free
@@ -219,7 +229,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __
     __shared__ int pp[kW / 2], pq[kW / 2];
     __shared__ double pc[kW / 2], ps[kW / 2];
     const int t = threadIdx.x;
-    sum_gram(part, nblk, b, S);
+    load_gram(gram, b, S);
     if (t < kW)
         for (int i = 0; i < kW; ++i) V[i][t] = i == t ? 1.0 : 0.0;
     __syncthreads();
@@ -231,6 +241,15 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __
     const int nb = (b + 1) & ~1, np = nb / 2;
     __shared__ double red[2][kJacobiThreads];
     __shared__ int stop;
+    // the round-robin schedule: round rd pairs the positions i and nb - 1 - i of the list
+    // (0, 1 + (rd mod (nb - 1)), ...), p < q
+    __shared__ uint8_t tp[kW][kW / 2], tq[kW][kW / 2];
+    for (int e = t; e < (nb - 1) * np; e += kJacobiThreads) {
+        const int rd = e / np, i0 = e - rd * np, i1 = nb - 1 - i0;
+        const int p = i0 == 0 ? 0 : 1 + (i0 - 1 + rd) % (nb - 1);
+        const int q = 1 + (i1 - 1 + rd) % (nb - 1);
+        tp[rd][i0] = (uint8_t)min(p, q), tq[rd][i0] = (uint8_t)max(p, q);
+    }
     for (int sweep = 0; sweep < 30; ++sweep) {
         // off-diagonal and diagonal squares: each thread sums a fixed set of entries, thread
         // 0 adds the per-thread sums in thread order
@@ -250,10 +269,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __
         if (stop) break;
         for (int rd = 0; rd < nb - 1; ++rd) {
             if (t < np) {
-                const int i0 = t, i1 = nb - 1 - t;
-                int p = i0 == 0 ? 0 : 1 + (i0 - 1 + rd) % (nb - 1);
-                int q = 1 + (i1 - 1 + rd) % (nb - 1);
-                if (p > q) { const int x = p; p = q; q = x; }
+                const int p = tp[rd][t], q = tq[rd][t];
                 double c = 1.0, sn = 0.0;
                 if (q < b) {
                     const double apq = S[p][q];
@@ -447,7 +463,7 @@ void launch_lowrank_factors(int N, int K, int r, int b, int iters, const float* 
     hipLaunchKernelGGL(gram_partial_kernel, gK, dim3(256), 0, st, (const float*)wk.Z, K, wk.part);
     hipLaunchKernelGGL(gram_sum_kernel, dim3(kW * kW / 64), dim3(256), 0, st, (const double*)wk.part, (int)gK.x,
                        wk.gsum);
-    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kJacobiThreads), 0, st, (const double*)wk.gsum, 1, b, wk.ub,
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kJacobiThreads), 0, st, (const double*)wk.gsum, b, wk.ub,
                        wk.sigma);
     const int64_t tot = (int64_t)N * r + (int64_t)r * K;
     hipLaunchKernelGGL(factors_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
