@@ -120,18 +120,25 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restri
 }
 
 // gsum[e] = sum of the partial Gram matrices part[k][e], so that the single-wave kernels
-// below read one 64 x 64 matrix.  A block takes 64 entries; its four waves sum consecutive
-// quarters of k in order, and the quarter sums are added in order (a fixed order).
-__global__ __launch_bounds__(256) void gram_sum_kernel(const double* __restrict__ part, int nblk,
-                                                       double* __restrict__ gsum) {
-    __shared__ double qs[4][64];
-    const int q = threadIdx.x >> 6, e = blockIdx.x * 64 + (threadIdx.x & 63);   // grid: kW * kW / 64
-    const int len = (nblk + 3) / 4, k0 = q * len, k1 = min(nblk, k0 + len);
+// below read one 64 x 64 matrix.  A block takes 64 entries; its eight waves sum consecutive
+// eighths of k in order, and the eighths are added in order (a fixed order).
+constexpr int kGramParts = 8;
+__global__ __launch_bounds__(64 * kGramParts) void gram_sum_kernel(const double* __restrict__ part, int nblk,
+                                                                   double* __restrict__ gsum) {
+    __shared__ double qs[kGramParts][64];
+    const int q = threadIdx.x >> 6, c = threadIdx.x & 63, e = blockIdx.x * 64 + c;   // grid: kW * kW / 64
+    const int len = (nblk + kGramParts - 1) / kGramParts, k0 = q * len, k1 = min(nblk, k0 + len);
     double s = 0.0;
+#pragma unroll 4
     for (int k = k0; k < k1; ++k) s += part[(int64_t)k * kW * kW + e];
-    qs[q][threadIdx.x & 63] = s;
+    qs[q][c] = s;
     __syncthreads();
-    if (q == 0) gsum[e] = ((qs[0][threadIdx.x] + qs[1][threadIdx.x]) + qs[2][threadIdx.x]) + qs[3][threadIdx.x];
+    if (q == 0) {
+        double v = qs[0][c];
+#pragma unroll
+        for (int i = 1; i < kGramParts; ++i) v += qs[i][c];
+        gsum[e] = v;
+    }
 }
 
 // A summed Gram matrix (64 x 64, b x b used) into LDS, zero outside b x b: threads t < 64
@@ -178,7 +185,8 @@ __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ par
     for (int j = 0; j < b; ++j) {
         // lanes i >= j: the column below the pivot (the pivot itself on lane j)
         double s = G[t < kW ? t : 0][j];
-        for (int k = 0; k < j; ++k) s -= L[t][k] * L[j][k];
+#pragma unroll 8
+        for (int k = 0; k < j; ++k) s -= L[t][k] * L[j][k];   // loads run ahead, sums in order
         __syncthreads();
         if (t == j) L[j][j] = s > 0.0 ? __builtin_sqrt(s) : 0.0;
         __syncthreads();
@@ -190,6 +198,7 @@ __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ par
         for (int i = t; i < b; ++i) {
             if (L[i][i] <= 0.0) continue;
             double s = i == t ? 1.0 : 0.0;
+#pragma unroll 8
             for (int k = t; k < i; ++k) s -= L[i][k] * Li[k][t];
             Li[i][t] = s / L[i][i];
         }
@@ -428,7 +437,7 @@ void orth(float* X, int rows, int b, const Work& w, hipStream_t st) {
     const int nblk = (rows + kGramRows - 1) / kGramRows;
     for (int pass = 0; pass < 2; ++pass) {   // CholeskyQR2
         hipLaunchKernelGGL(gram_partial_kernel, dim3(nblk), dim3(256), 0, st, (const float*)X, rows, w.part);
-        hipLaunchKernelGGL(gram_sum_kernel, dim3(kW * kW / 64), dim3(256), 0, st, (const double*)w.part, nblk,
+        hipLaunchKernelGGL(gram_sum_kernel, dim3(kW * kW / 64), dim3(64 * kGramParts), 0, st, (const double*)w.part, nblk,
                            w.gsum);
         hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(64), 0, st, (const double*)w.gsum, 1, b, w.rinv);
         hipLaunchKernelGGL(apply_rinv_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, X, rows,
@@ -461,7 +470,7 @@ void launch_lowrank_factors(int N, int K, int r, int b, int iters, const float* 
     }
     skinny<true>(w, smooth_inv, N, K, wk.Q, wk.Z, wk, st);
     hipLaunchKernelGGL(gram_partial_kernel, gK, dim3(256), 0, st, (const float*)wk.Z, K, wk.part);
-    hipLaunchKernelGGL(gram_sum_kernel, dim3(kW * kW / 64), dim3(256), 0, st, (const double*)wk.part, (int)gK.x,
+    hipLaunchKernelGGL(gram_sum_kernel, dim3(kW * kW / 64), dim3(64 * kGramParts), 0, st, (const double*)wk.part, (int)gK.x,
                        wk.gsum);
     hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kJacobiThreads), 0, st, (const double*)wk.gsum, b, wk.ub,
                        wk.sigma);
