@@ -170,17 +170,23 @@ __device__ void sum_gram(const double* part, int nblk, int b, double (*G)[kW + 1
     __syncthreads();
 }
 
-// CholeskyQR step: G = L L^T; rinv = L^-T (upper triangular, b x b, zero elsewhere), so that
-// X rinv has orthonormal columns.  A pivot that is not positive (a rank-deficient block)
-// zeroes its column.  One wave of 64 lanes.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// CholeskyQR step, factorization: G = L L^T.  Writes lt = L^T (64 x 64, binary64, zero
+// outside b x b) and invd[i] = 1 / L[i][i] (0 where the pivot is not positive: a
+// rank-deficient block, whose column then drops out).  One wave of 64 lanes.
 __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ part, int nblk, int b,
-                                                  float* __restrict__ rinv) {
+                                                  double* __restrict__ lt, double* __restrict__ invd) {
     __shared__ double G[kW][kW + 1];   // padded: column walks stay conflict-free
     __shared__ double L[kW][kW + 1];   // padded: column walks stay conflict-free
-    __shared__ double Li[kW][kW + 1];   // padded: column walks stay conflict-free
     const int t = threadIdx.x;
     sum_gram(part, nblk, b, G);
-    for (int i = 0; i < kW; ++i) L[i][t] = 0.0, Li[i][t] = 0.0;
+    for (int i = 0; i < kW; ++i) L[i][t] = 0.0;
     __syncthreads();
     for (int j = 0; j < b; ++j) {
         // lanes i >= j: the column below the pivot (the pivot itself on lane j)
@@ -193,37 +199,35 @@ __global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ par
         if (t > j && t < b) L[t][j] = L[j][j] > 0.0 ? s / L[j][j] : 0.0;
         __syncthreads();
     }
-    // column t of L^-1 by forward substitution
-    if (t < b && L[t][t] > 0.0) {
-        for (int i = t; i < b; ++i) {
-            if (L[i][i] <= 0.0) continue;
-            double s = i == t ? 1.0 : 0.0;
-#pragma unroll 8
-            for (int k = t; k < i; ++k) s -= L[i][k] * Li[k][t];
-            Li[i][t] = s / L[i][i];
-        }
-    }
-    __syncthreads();
-    for (int i = 0; i < kW; ++i) rinv[i * kW + t] = (float)Li[t][i];   // rinv[i][j] = Li[j][i]
+    for (int k = 0; k < kW; ++k) lt[k * kW + t] = L[t][k];   // lt[k][t] = L[t][k]
+    invd[t] = t < b && L[t][t] > 0.0 ? 1.0 / L[t][t] : 0.0;
 }
 
-// X <- X rinv (four rows per block)
-__global__ __launch_bounds__(256) void apply_rinv_kernel(float* __restrict__ X, int rows,
-                                                         const float* __restrict__ rinv) {
-    __shared__ float R[kW][kW];
-    __shared__ float xs[4][kW];
-    const int tid = threadIdx.x, rr = tid >> 6, j = tid & 63;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int idx = tid + 256 * e;
-        R[idx >> 6][idx & 63] = rinv[idx];
-    }
-    const int64_t r = (int64_t)blockIdx.x * 4 + rr;
-    xs[rr][j] = r < rows ? X[r * kW + j] : 0.0f;
+// X <- X L^-T row by row (the CholeskyQR step's orthonormalization): y L^T = x, i.e.
+// y_i = (x_i - sum_{k<i} L[i][k] y_k) / L[i][i] in binary64, 0 where the pivot is not
+// positive.  One wave per row, lane j holding x_j: step i takes y_i from lane i and subtracts
+// L[j][i] y_i from the lanes j > i, so each x_j gets its terms in increasing i.  Sixteen rows
+// per block share L^T in LDS.
+constexpr int kSolveRows = 16;
+__global__ __launch_bounds__(64 * kSolveRows) void solve_rows_kernel(float* __restrict__ X, int rows, int b,
+                                                                     const double* __restrict__ lt,
+                                                                     const double* __restrict__ invd) {
+    __shared__ double Lt[kW][kW];   // Lt[i][j] = L[j][i]
+    __shared__ double id[kW];
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int e = tid; e < kW * kW; e += 64 * kSolveRows) Lt[e >> 6][e & 63] = lt[e];
+    if (tid < kW) id[tid] = invd[tid];
     __syncthreads();
-    float s = 0.0f;
-    for (int i = 0; i < kW; ++i) s = fmaf(xs[rr][i], R[i][j], s);
-    if (r < rows) X[r * kW + j] = s;
+    const int64_t r = (int64_t)blockIdx.x * kSolveRows + (tid >> 6);
+    if (r >= rows) return;   // a whole wave
+    double x = X[r * kW + lane];
+    double y = 0.0;
+    for (int i = 0; i < b; ++i) {
+        const double yi = readlane_f64(x, i) * id[i];
+        if (lane == i) y = yi;
+        if (lane > i) x -= Lt[i][lane] * yi;
+    }
+    X[r * kW + lane] = (float)y;
 }
 
 // Z^T Z = U_B diag(sigma^2) U_B^T by cyclic Jacobi (binary64, kJacobiThreads threads: the
@@ -393,8 +397,8 @@ __global__ __launch_bounds__(256) void pad_kernel(const float* __restrict__ src,
 constexpr int kSlices = 20;  // inner-dimension slices of a skinny product (enough blocks to fill the GPU)
 
 struct Work {
-    float *Q, *Z, *rinv, *ub, *sigma, *slices;
-    double *part, *gsum;
+    float *Q, *Z, *ub, *sigma, *slices;
+    double *part, *gsum, *lt, *invd;
 };
 
 Work carve(void* ws, int N, int K) {
@@ -411,8 +415,10 @@ Work carve(void* ws, int N, int K) {
     p += (int64_t)N * kW * 4;
     w.Z = (float*)p;
     p += (int64_t)K * kW * 4;
-    w.rinv = (float*)p;
-    p += kW * kW * 4;
+    w.lt = (double*)p;
+    p += kW * kW * 8;
+    w.invd = (double*)p;
+    p += kW * 8;
     w.ub = (float*)p;
     p += kW * kW * 4;
     w.sigma = (float*)p;
@@ -439,9 +445,9 @@ void orth(float* X, int rows, int b, const Work& w, hipStream_t st) {
         hipLaunchKernelGGL(gram_partial_kernel, dim3(nblk), dim3(256), 0, st, (const float*)X, rows, w.part);
         hipLaunchKernelGGL(gram_sum_kernel, dim3(kW * kW / 64), dim3(64 * kGramParts), 0, st, (const double*)w.part, nblk,
                            w.gsum);
-        hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(64), 0, st, (const double*)w.gsum, 1, b, w.rinv);
-        hipLaunchKernelGGL(apply_rinv_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, X, rows,
-                           (const float*)w.rinv);
+        hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(64), 0, st, (const double*)w.gsum, 1, b, w.lt, w.invd);
+        hipLaunchKernelGGL(solve_rows_kernel, dim3((unsigned)((rows + kSolveRows - 1) / kSolveRows)),
+                           dim3(64 * kSolveRows), 0, st, X, rows, b, (const double*)w.lt, (const double*)w.invd);
     }
 }
 
@@ -450,7 +456,7 @@ void orth(float* X, int rows, int b, const Work& w, hipStream_t st) {
 int64_t lowrank_workspace_bytes(int N, int K) {
     const int nblk = (std::max(N, K) + kGramRows - 1) / kGramRows;
     return (int64_t)(nblk + 1) * kW * kW * 8 + (int64_t)kSlices * std::max(N, K) * kW * 4 +
-           (int64_t)(N + K) * kW * 4 + 2 * kW * kW * 4 + kW * 4;
+           (int64_t)(N + K) * kW * 4 + kW * kW * 8 + kW * 8 + kW * kW * 4 + kW * 4;
 }
 
 void launch_lowrank_factors(int N, int K, int r, int b, int iters, const float* w,
