@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __
     // pairs of a round are disjoint.  Each round takes every pair's rotation from S as the
     // round finds it, then applies all of them: columns (S and V), then rows.
     const int nb = (b + 1) & ~1, np = nb / 2;
-    __shared__ double red[2][kJacobiThreads];
+    __shared__ double red[2][kJacobiThreads], red2[2][32];
     __shared__ int stop;
     // the round-robin schedule: round rd pairs the positions i and nb - 1 - i of the list
     // (0, 1 + (rd mod (nb - 1)), ...), p < q
@@ -264,8 +264,8 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __
         tp[rd][i0] = (uint8_t)min(p, q), tq[rd][i0] = (uint8_t)max(p, q);
     }
     for (int sweep = 0; sweep < 30; ++sweep) {
-        // off-diagonal and diagonal squares: each thread sums a fixed set of entries, thread
-        // 0 adds the per-thread sums in thread order
+        // off-diagonal and diagonal squares: each thread sums a fixed set of entries; the
+        // per-thread sums are added in a fixed order
         double off = 0.0, dia = 0.0;
         for (int e = t; e < b * b; e += kJacobiThreads) {
             const int i = e / b, j = e - i * b;
@@ -273,9 +273,16 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* __
         }
         red[0][t] = off, red[1][t] = dia;
         __syncthreads();
+        if (t < 32) {   // 32 runs of consecutive threads, each summed in order, then the runs
+            double o = 0.0, d = 0.0;
+            for (int k = 0; k < kJacobiThreads / 32; ++k) o += red[0][t * (kJacobiThreads / 32) + k],
+                                                           d += red[1][t * (kJacobiThreads / 32) + k];
+            red2[0][t] = o, red2[1][t] = d;
+        }
+        __syncthreads();
         if (t == 0) {
             double o = 0.0, d = 0.0;
-            for (int k = 0; k < kJacobiThreads; ++k) o += red[0][k], d += red[1][k];
+            for (int k = 0; k < 32; ++k) o += red2[0][k], d += red2[1][k];
             stop = o <= 1e-24 * d;
         }
         __syncthreads();
