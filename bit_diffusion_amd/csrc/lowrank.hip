@@ -8,8 +8,8 @@
 //   U = Q U_B, V = Z U_B diag(1 / sigma);  l1 = bf16(sqrt(sigma) V^T diag(smooth_inv)),
 //   l2 = bf16(U sqrt(sigma)).
 // The skinny products are LDS-tiled fp32 kernels; orth is CholeskyQR2 with the Gram matrix
-// summed in binary64; the small symmetric eigenproblem is cyclic Jacobi on one wave in
-// binary64.  Tall matrices are stored with 64 columns (the block width), columns past b zero.
+// summed in binary64 and the rows solved against its Cholesky factor in binary64; the small
+// symmetric eigenproblem is cyclic Jacobi in binary64 on one workgroup.  Tall matrices are stored with 64 columns (the block width), columns past b zero.
 #include <algorithm>
 
 #include "common.hpp"
