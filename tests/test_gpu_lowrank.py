@@ -71,6 +71,25 @@ def test_lowrank_exact_rank(N, K):
     assert e <= 1e-2
 
 
+@pytest.mark.parametrize("b,r,N,K", [(16, 16, 200, 320), (33, 32, 264, 448), (64, 48, 384, 640)])
+def test_lowrank_block_widths_exact_rank(b, r, N, K):
+    """Block widths 16, 33 (odd: the eigensolver's round-robin schedule gets a dummy index)
+    and 64 (the maximum) on a weight of rank b: the b-column block spans its range, so the
+    leading r singular values are the exact SVD's up to fp32."""
+    rng = np.random.default_rng(1800 + b)
+    x = synth.random_bf16(rng, (256, K), 1.0)
+    k = b
+    w = rng.normal(0, 0.02, (N, k)) @ rng.normal(0, 1.0, (k, K)) / np.sqrt(k)
+    w32 = w.astype(np.float32)
+    w64 = w32.astype(np.float64)
+    si, lam = smoothing(x, w64)
+    _, _, sig = _factor(w32, si, r, b, 1, rng)
+    s_ex = np.linalg.svd(w64 * lam[None, :], compute_uv=False)[:r]
+    rel = np.max(np.abs(sig - s_ex) / s_ex)
+    print(f"b={b} rank {k}: sigma rel err {rel:.2e}")
+    assert rel <= 1e-4
+
+
 def test_lowrank_decaying_spectrum():
     rng = np.random.default_rng(1710)
     w32, w64, si, lam = _case(rng, 384, 512, "decay")
