@@ -1,9 +1,10 @@
-// quant_lane.hpp -- the per-lane steps of the INT4 activation quantizer on gfx950, shared
-// by the activation kernel and the GEMM epilogue that quantizes the next layer's input.
-// A lane holds 32 consecutive channels of one row (one half of a 64-channel group): the
-// lane of one FP6 MFMA fragment of packed_layout.hpp.  The quantizer is defined as a
-// sequence of individually rounded fp32 operations (page "Hugging Face 把 Nunchaku 4-bit
-// Diffusion 接到 Diffusers", 技术细节 1 step 3): s = absmax / 7, q = rne(x_hat / s).
+// quant_lane.hpp -- the per-lane steps of the 4-bit quantizers on gfx950: INT4 (shared by
+// the activation kernel and the GEMM epilogue that quantizes the next layer's input) and
+// NVFP4 (shared by the activation kernel and the weight quantizer).  A lane holds 32
+// consecutive channels of one row (one half of a 64-channel group): the lane of one FP6
+// MFMA fragment of packed_layout.hpp.  The quantizers are defined as sequences of
+// individually rounded fp32 operations (page "Hugging Face 把 Nunchaku 4-bit Diffusion 接到
+// Diffusers", 技术细节 1 step 3 and 技术细节 3): INT4 s = absmax / 7, q = rne(x_hat / s).
 #pragma once
 
 #include <stdint.h>
