@@ -215,9 +215,11 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 sc) {
     return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-__device__ __forceinline__ f16x2 scale_pair(uint32_t sc, int byte) {
-    const _Float16 v = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)(sc >> (8 * byte)), 0);
-    return f16x2{v, v};
+// Bytes 2h and 2h + 1 of sc (the two E4M3 block scales lane half h needs in a sub-stage)
+// as f16, exact: every E4M3 value is an f16 value, and a scale operand of 1 leaves the
+// conversion unscaled.
+__device__ __forceinline__ f16x2 scale_pair(uint32_t sc, int h) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc >> (16 * h), 1.0f, false);
 }
 
 // The output tile through LDS: each wave writes its 32 x 96 half-tiles to its own region
@@ -337,16 +339,18 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
             const int row = wm * 64 + 32 * i + fr;
             ca[i] = *reinterpret_cast<const uint4*>(st + row * 128 + 16 * ((2 * u + fh) ^ ((row >> 1) & 7)));
             const uint32_t sc = *reinterpret_cast<const uint32_t*>(st + kCA + kCB + 16 * row + su);
-            sa[i][0] = scale_pair(sc, 2 * fh);
-            sa[i][1] = scale_pair(sc, 2 * fh + 1);
+            const f16x2 pr = scale_pair(sc, fh);
+            sa[i][0] = f16x2{pr[0], pr[0]};
+            sa[i][1] = f16x2{pr[1], pr[1]};
         }
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const int row = wn * 96 + 32 * j + fr;
             cb[j] = *reinterpret_cast<const uint4*>(st + kCA + row * 128 + 16 * ((2 * u + fh) ^ ((row >> 1) & 7)));
             const uint32_t sc = *reinterpret_cast<const uint32_t*>(st + kCA + kCB + kSA + 16 * row + su);
-            sb[j][0] = scale_pair(sc, 2 * fh);
-            sb[j][1] = scale_pair(sc, 2 * fh + 1);
+            const f16x2 pr = scale_pair(sc, fh);
+            sb[j][0] = f16x2{pr[0], pr[0]};
+            sb[j][1] = f16x2{pr[1], pr[1]};
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
