@@ -264,6 +264,17 @@ __device__ __forceinline__ void store_tile_staged(const f32x16 (&acc)[2][3], uin
     }
 }
 
+// Stores per wave of the LDS-staged bf16 epilogue of a whole tile: 2 halves x 6 row segments.
+constexpr int kStagedStoresBf16 = 2 * (32 * (96 * 2 / 16) / 64);
+static_assert(8 * 32 * 208 <= kFStage, "the bf16 staging area fits in one stage buffer");
+
+// Persistent: workgroup b takes tiles b, b + gridDim.x, ...  With a bf16 output staged
+// through LDS, the first stage of the next tile is copied into the free stage buffer while
+// the last stage of the current tile computes, and the output goes out through the other
+// buffer; the next tile's first wait then lets the epilogue's stores stay in flight (vector
+// memory operations complete in issue order, so once at most kStagedStoresBf16 are
+// outstanding, the earlier copies have landed).  Other outputs copy the next tile's first
+// stage after a barrier, as a new workgroup would.
 __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p) {
     extern __shared__ __align__(16) uint8_t fsm[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -274,61 +285,61 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
     const int S = K / kFK;
     const int64_t num_m = (M + kFM - 1) / kFM;
     const int num_n = (N + kFN - 1) / kFN;
-    // tiles in row-major order; the workgroups of one XCD (ids congruent mod 8) take a
-    // contiguous range of them when the count allows
-    int64_t t = blockIdx.x;
     const int64_t nt = num_m * num_n;
-    if ((nt & 7) == 0) t = (t & 7) * (nt >> 3) + (t >> 3);
-    const int64_t m0 = (t / num_n) * kFM;
-    const int n0 = (int)(t % num_n) * kFN;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(flds_u8*)fsm);
+    const int esz = p.out_bf16 ? 2 : 4;
+    const bool staged = ((int64_t)N * esz) % 16 == 0 && (reinterpret_cast<uintptr_t>(p.out) % 16) == 0;
+    const bool chain = staged && p.out_bf16;
 
     const uint8_t* acodes = (const uint8_t*)p.acodes;
     const uint8_t* wcodes = (const uint8_t*)p.wcodes;
     const uint8_t* ascales = (const uint8_t*)p.ascales;
     const uint8_t* wscales = (const uint8_t*)p.wscales;
 
-    // ---- copies of stage s: 56 code copies (8 rows x 128 bytes each: 32 for A, 24 for B)
-    // and 7 scale copies (16 bytes per row, 64 rows each: 4 for A, 3 for B); wave w issues
-    // numbers w, w + 8, ...
-    auto issue = [&](int s) {
-        const uint32_t base = lds0 + (s & 1) * kFStage;
-        const int kc = s * kFK;                       // first channel of the stage
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int d = wave + 8 * q;
-            if (d < 56) {
-                const bool isa = d < 32;
-                const int j = isa ? d : d - 32;
-                const int row = 8 * j + (lane >> 3), pos = lane & 7;
-                const int c = pos ^ ((row >> 1) & 7);
-                const uint8_t* src = isa ? acodes + min(m0 + row, M - 1) * (K / 2)
-                                         : wcodes + (int64_t)min(n0 + row, N - 1) * (K / 2);
-                fdma_x4(src + kc / 2 + 16 * c, base + (isa ? 0 : kCA) + 1024 * j);
-            } else if (d < 63) {
-                const int v = d - 56;                 // 0-3 A, 4-6 B
-                const bool isa = v < 4;
-                const int row = 64 * (isa ? v : v - 4) + lane;
-                const uint8_t* src = isa ? ascales + min(m0 + row, M - 1) * (K / 16)
-                                         : wscales + (int64_t)min(n0 + row, N - 1) * (K / 16);
-                fdma_x4(src + kc / 16, base + kCA + kCB + (isa ? 1024 * v : kSA + 1024 * (v - 4)));
-            }
-        }
+    // tiles in row-major order; the workgroups of one XCD (ids congruent mod 8) take a
+    // contiguous range of them when the count allows (gridDim.x is a multiple of 8 or nt)
+    auto tile_origin = [&](int64_t tile, int64_t& m0, int& n0) {
+        int64_t t = tile;
+        if ((nt & 7) == 0) t = (t & 7) * (nt >> 3) + (t >> 3);
+        m0 = (t / num_n) * kFM;
+        n0 = (int)(t % num_n) * kFN;
     };
 
-    f32x16 acc[2][3];
+    // ---- copies of one stage: 56 code copies (8 rows x 128 bytes each: 32 for A, 24 for
+    // B) and 7 scale copies (16 bytes per row, 64 rows each: 4 for A, 3 for B).  Wave w
+    // copies code rows 8 j .. 8 j + 7 of A for j = w + 8 q (q < 4) and of B for j = w + 8 q
+    // (q < 3), and scale rows 64 w .. of A (w < 4) or 64 (w - 4) .. of B (w = 4..6).  Lane l
+    // of a code copy takes row 8 j + l / 8 and stores its chunk c at position l % 8, i.e.
+    // chunk c = (l % 8) ^ ((row / 2) % 8), which is the same for every j of the wave.
+    const int lrow = lane >> 3;
+    const int c16 = 16 * ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
+    // first source byte of each of the wave's copies for a tile (stage 0)
+    auto tile_src = [&](int64_t m0, int n0, const uint8_t* (&src)[8]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int q = 0; q < 4; ++q)
+            src[q] = acodes + min(m0 + 8 * (wave + 8 * q) + lrow, M - 1) * (K / 2) + c16;
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int q = 0; q < 3; ++q)
+            src[4 + q] = wcodes + (int64_t)min(n0 + 8 * (wave + 8 * q) + lrow, N - 1) * (K / 2) + c16;
+        src[7] = wave < 4 ? ascales + min(m0 + 64 * wave + lane, M - 1) * (K / 16)
+                          : wscales + (int64_t)min(n0 + 64 * (wave - 4) + lane, N - 1) * (K / 16);
+    };
+    // the copies of the stage starting at channel kc into buffer b
+    auto issue = [&](const uint8_t* const (&src)[8], int kc, int b) {
+        const uint32_t base = lds0 + b * kFStage;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        for (int q = 0; q < 4; ++q) fdma_x4(src[q] + kc / 2, base + 1024 * (wave + 8 * q));
+#pragma unroll
+        for (int q = 0; q < 3; ++q) fdma_x4(src[4 + q] + kc / 2, base + kCA + 1024 * (wave + 8 * q));
+        if (wave < 7) fdma_x4(src[7] + kc / 16, base + kCA + kCB + 1024 * wave);
+    };
 
     // ---- compute one 64-channel sub-stage u of stage buffer b.  The MFMA contracts any
     // consistent permutation of the channels: for k-step kk, lane half h supplies codes
     // 8 (4h + kk) .. + 7 of the sub-stage, i.e. dword kk of its 16-byte chunk 2u + h, in
     // block 2h + kk / 2.
     const int fr = lane & 31, fh = lane >> 5;
+    f32x16 acc[2][3];
     auto compute = [&](int b, int u) {
         const uint8_t* st = fsm + b * kFStage;
         const int su = 4 * u;   // this sub-stage's 4 scale bytes within the row's 16
@@ -373,75 +384,154 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
         }
     };
 
-    // ---- pipeline: two stage buffers; stage s + 1 is copied while stage s computes
-    issue(0);
-    for (int s = 0; s < S; ++s) {
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0): this wave's copies of s landed
-        fbarrier();                           // every wave's have; buffer (s + 1) & 1 is free
-        if (s + 1 < S) issue(s + 1);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) compute(s & 1, u);
-    }
+    int gs = 0;                 // stages this workgroup has run (buffer of stage s: (gs + s) & 1)
+    bool ahead = false;         // the current tile's first stage is already copied
+    bool stores_out = false;    // the previous tile's staged stores may still be in flight
+    for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
+        int64_t m0;
+        int n0;
+        tile_origin(tile, m0, n0);
+        const int64_t next = tile + gridDim.x;
+        int64_t nm0 = 0;
+        int nn0 = 0;
+        if (next < nt) tile_origin(next, nm0, nn0);
 
-    // ---- epilogue: S_a S_w, low-rank branch, bias, GELU, store
-    const float sasw = p.Sa * p.Sw;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+            for (int j = 0; j < 3; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] *= sasw;
-    const uint16_t* lora = (const uint16_t*)p.lora;
-    const uint16_t* l2 = (const uint16_t*)p.l2;
-    const int r = p.r;
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+        const uint8_t* src[8];
+        tile_src(m0, n0, src);
+        if (!ahead) {
+            if (tile != blockIdx.x) fbarrier();   // every wave is done with the last epilogue's LDS
+            issue(src, 0, gs & 1);
+        }
+        // ---- pipeline: two stage buffers; stage s + 1 is copied while stage s computes, and
+        // when chained the last stage copies the next tile's first
+        for (int s = 0; s < S; ++s) {
+            if (s == 0 && stores_out)
+                __builtin_amdgcn_s_waitcnt(0x0070 | kStagedStoresBf16);   // vmcnt(12), lgkmcnt(0)
+            else
+                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0): this wave's copies of s landed
+            fbarrier();                           // every wave's have; buffer (gs + s + 1) & 1 is free
+            if (s + 1 < S) {
+                issue(src, (s + 1) * kFK, (gs + s + 1) & 1);
+            } else if (chain && next < nt) {
+                int64_t cm0 = nm0;
+                int cn0 = nn0;
+                asm volatile("" : "+s"(cm0), "+s"(cn0));   // keeps these addresses out of the loop
+                const uint8_t* nsrc[8];
+                tile_src(cm0, cn0, nsrc);
+                issue(nsrc, 0, (gs + S) & 1);
+            }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t mrow = min(m0 + wm * 64 + i * 32 + fr, M - 1);
+            for (int u = 0; u < 4; ++u) compute((gs + s) & 1, u);
+        }
+        const int last = (gs + S - 1) & 1;
+        ahead = chain && next < nt;
+        stores_out = false;
+        gs += S;
+
+        // ---- epilogue: S_a S_w, low-rank branch, bias, GELU, store.  Its lane-dependent
+        // addresses start from an opaque copy of the lane index, so that they are formed here
+        // and not kept in registers through the main loop.
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int efr = el & 31, efh = el >> 5;
+        const float sasw = p.Sa * p.Sw;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] *= sasw;
+        const uint16_t* lora = (const uint16_t*)p.lora;
+        const uint16_t* l2 = (const uint16_t*)p.l2;
+        const int r = p.r;
+        // the operands of 32 ranks are loaded together, then contracted (per accumulator in
+        // rank order), so the loads of a chunk wait for memory once
+        const uint16_t* ar[2];
+        const uint16_t* br[3];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ar[i] = lora + min(m0 + wm * 64 + i * 32 + efr, M - 1) * r + 8 * efh;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) br[j] = l2 + (int64_t)min(n0 + wn * 96 + j * 32 + efr, N - 1) * r + 8 * efh;
+        int kk = 0;
+        for (; kk + 32 <= r; kk += 32) {
+            uint4 va[2][2], vb[3][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) va[i][h] = *reinterpret_cast<const uint4*>(ar[i] + kk + 16 * h);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) vb[j][h] = *reinterpret_cast<const uint4*>(br[j] + kk + 16 * h);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // every load issued before the first MFMA
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[i][h]), as_bf16x8(vb[j][h]),
+                                                                          acc[i][j], 0, 0, 0);
+        }
+        if (kk < r) {   // 16 ranks left
+            uint4 va[2], vb[3];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) va[i] = *reinterpret_cast<const uint4*>(ar[i] + kk);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) vb[j] = *reinterpret_cast<const uint4*>(br[j] + kk);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[i]), as_bf16x8(vb[j]), acc[i][j], 0, 0, 0);
+        }
+        const uint16_t* bias = (const uint16_t*)p.bias;
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
-            const int ncol = min(n0 + wn * 96 + j * 32 + fr, N - 1);
-            for (int kk = 0; kk < r; kk += 16) {
-                const uint4 va = *reinterpret_cast<const uint4*>(lora + mrow * r + kk + 8 * fh);
-                const uint4 vb = *reinterpret_cast<const uint4*>(l2 + (int64_t)ncol * r + kk + 8 * fh);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(vb), acc[i][j], 0, 0, 0);
-            }
-        }
-    }
-    const uint16_t* bias = (const uint16_t*)p.bias;
+            const int col = n0 + wn * 96 + j * 32 + efr;
+            const float bv = (bias && col < N) ? bf16_to_f32(bias[col]) : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int col = n0 + wn * 96 + j * 32 + fr;
-        const float bv = (bias && col < N) ? bf16_to_f32(bias[col]) : 0.0f;
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float v = acc[i][j][e] + bv;
-                if (p.act == 1) v = gelu_tanh(v);
-                acc[i][j][e] = v;
-            }
-    }
-    const int esz = p.out_bf16 ? 2 : 4;
-    if (((int64_t)N * esz) % 16 == 0 && (reinterpret_cast<uintptr_t>(p.out) % 16) == 0) {
-        fbarrier();   // every wave is done with the stage buffers
-        if (p.out_bf16) store_tile_staged<true>(acc, fsm, p, m0, n0, wave, wm, wn, lane);
-        else store_tile_staged<false>(acc, fsm, p, m0, n0, wave, wm, wn, lane);
-        return;
-    }
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int col = n0 + wn * 96 + j * 32 + fr;
-        if (col >= N) continue;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-                if (row < M) {
-                    if (p.out_bf16) ((uint16_t*)p.out)[row * N + col] = (uint16_t)f32_to_bf16(acc[i][j][e]);
-                    else ((float*)p.out)[row * N + col] = acc[i][j][e];
+                for (int e = 0; e < 16; ++e) {
+                    float v = acc[i][j][e] + bv;
+                    if (p.act == 1) v = gelu_tanh(v);
+                    acc[i][j][e] = v;
                 }
+        }
+        if (staged) {
+            fbarrier();   // every wave is done with the last stage's buffer
+            if (p.out_bf16) {
+                store_tile_staged<true>(acc, fsm + last * kFStage, p, m0, n0, wave, wm, wn, el);
+                // a whole tile issues every one of its stores; a partial one may skip some
+                stores_out = ahead && m0 + kFM <= M && n0 + kFN <= N;
+            } else {
+                store_tile_staged<false>(acc, fsm, p, m0, n0, wave, wm, wn, el);
             }
+            continue;
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int col = n0 + wn * 96 + j * 32 + efr;
+            if (col >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * efh + (e & 3);
+                    if (row < M) {
+                        if (p.out_bf16) ((uint16_t*)p.out)[row * N + col] = (uint16_t)f32_to_bf16(acc[i][j][e]);
+                        else ((float*)p.out)[row * N + col] = acc[i][j][e];
+                    }
+                }
+        }
     }
 }
 
@@ -465,8 +555,11 @@ void launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
     const int64_t num_m = (a.M + kFM - 1) / kFM;
     const int num_n = (a.N + kFN - 1) / kFN;
     if (fast && num_m * num_n < ((int64_t)1 << 31) && gemm_nvfp4_init()) {
-        hipLaunchKernelGGL(gemm_nvfp4_f16_kernel, dim3((unsigned)(num_m * num_n)), dim3(kFThreads),
-                           kFSmemBytes, st, a);
+        // one workgroup per CU (the LDS of two stage buffers allows no more), each taking
+        // every grid-th tile; a multiple of 8 keeps each XCD on its own range of tiles
+        const int64_t nt = num_m * num_n;
+        const int64_t grid = std::min<int64_t>(nt, std::max(8, cu_count() / 8 * 8));
+        hipLaunchKernelGGL(gemm_nvfp4_f16_kernel, dim3((unsigned)grid), dim3(kFThreads), kFSmemBytes, st, a);
         return;
     }
     dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));

@@ -114,6 +114,36 @@ def test_gemm_nvfp4_shapes(M, N, K, r, bias, act):
     gu.assert_bf16_close(yb, ref, cond, gu.nvfp4_nround(K, r), gelu=act == 1)
 
 
+def test_gemm_nvfp4_tiles_per_workgroup():
+    """More 256 x 192 tiles (9 x 32) than compute units, so a workgroup of the fast kernel
+    takes several tiles in turn (with a bf16 output, the next tile's first stage is copied
+    during the current tile's last one), with ragged last tile rows and columns; GELU,
+    bias and rank 32, both output types.  Sampled against the oracle: random points, every
+    column of the first, middle and last rows, every row of the first and last columns."""
+    M, N, K, r = 2100, 6050, 512, 32
+    rng = np.random.default_rng(77)
+    ca, cw = synth.random_packed_nibbles(rng, M, K), synth.random_packed_nibbles(rng, N, K)
+    sa = rng.integers(0, 0x7F, size=(M, K // 16)).astype(np.uint8)
+    sw = rng.integers(0, 0x7F, size=(N, K // 16)).astype(np.uint8)
+    Sa, Sw = np.float32(0.003), np.float32(0.0007)
+    lora = synth.random_bf16(rng, (M, r), 1.0)
+    l2 = synth.random_bf16(rng, (N, r), 0.1)
+    b = synth.random_bf16(rng, (N,), 0.3)
+    mi = rng.integers(0, M, 3000)
+    ni = rng.integers(0, N, 3000)
+    rows, cols = np.array([0, M // 2, M - 1]), np.array([0, N - 1])
+    mi = np.concatenate([mi, np.repeat(rows, N), np.tile(np.arange(M), len(cols))])
+    ni = np.concatenate([ni, np.tile(np.arange(N), len(rows)), np.repeat(cols, M)])
+    ref = oracle.gemm_w4a4_nvfp4_at(mi, ni, ca, sa, Sa, cw, sw, Sw, lora, l2, b, 1)
+    cond = gu.nvfp4_cond(ca, sa, Sa, cw, sw, Sw, lora, l2, b, mi, ni)
+    nr = gu.nvfp4_nround(K, r)
+    y = gu.host(gu.gemm(ca, sa, cw, sw, lora, l2, b, 1, False, "nvfp4", Sa, Sw))
+    assert gu.rel_fro(y[mi, ni], ref) <= 1e-5
+    gu.assert_f32_within(y[mi, ni], ref, cond, nr, gelu=True)
+    yb = gu.host(gu.gemm(ca, sa, cw, sw, lora, l2, b, 1, True, "nvfp4", Sa, Sw))
+    gu.assert_bf16_close(yb[mi, ni], ref, cond, nr, gelu=True)
+
+
 def test_gemm_nvfp4_unaligned_scales():
     """E4M3 scale arrays that are not 16-byte aligned are accepted (they take the reference
     kernel)."""
