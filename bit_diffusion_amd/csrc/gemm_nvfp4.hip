@@ -8,16 +8,17 @@
 // cannot carry NVFP4's E4M3 scales on 16-element blocks.  Instead each E2M1 value (at
 // most 2 significant bits) is multiplied by its E4M3 block scale (at most 4 significant
 // bits): the product has at most 6 significant bits and lies in [2^-10, 2688], so it is
-// exact in f16 (and in bf16).  The operands are dequantized once per pipeline stage into
-// LDS and contracted with the 16-bit MFMA in fp32; S_a * S_w is applied in the epilogue.
+// exact in f16 (and in bf16).  The products are formed in registers right before the
+// 16-bit MFMA that contracts them in fp32; S_a * S_w is applied in the epilogue.
 //
 // Fast kernel (gemm_nvfp4_f16_kernel): 256x192 output tile per 512-thread workgroup, 8
-// waves as 4 x 2 of 64x96.  Codes and scale bytes go to LDS by LDS DMA in stages of 256
-// channels (128 contiguous bytes of codes per row: whole cache lines), double-buffered,
-// one barrier per stage.  Each wave converts the operands of its own MFMA fragments per
-// 16-channel k-step: v_cvt_scalef32_pk_f16_fp4 (scale 1) turns a code byte into two exact
-// f16 values and v_pk_mul_f16 applies the block scale (exact); v_mfma_f32_32x32x16_f16
-// contracts.
+// waves as 4 x 2 of 64x96; one workgroup per CU, each taking every grid-th tile, tiles
+// numbered down bands of 4 tile rows.  Codes and scale bytes go to LDS by LDS DMA in stages
+// of 256 channels (128 contiguous bytes of codes per row: whole cache lines),
+// double-buffered, one barrier per stage.  Each wave converts the operands of its own MFMA
+// fragments per 16-channel k-step: v_cvt_scalef32_pk_f16_fp4 (scale 1) turns a code byte
+// into two exact f16 values and v_pk_mul_f16 applies the block scale (exact);
+// v_mfma_f32_32x32x16_f16 contracts.
 #include "common.hpp"
 #include "launch.hpp"
 
