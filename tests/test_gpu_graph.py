@@ -120,3 +120,55 @@ def test_fused_mlp_graph_replays():
         assert torch.equal(npk, e_pk), f"replay {k}: packed codes differ"
         assert torch.equal(nsc.view(torch.int32), e_sc.view(torch.int32)), f"replay {k}: scales differ"
         assert np.array_equal(gu.host(nlora), e_lo), f"replay {k}: lora_act differs"
+
+
+@pytest.mark.parametrize("out_dtype", [1, 0])
+def test_nvfp4_linear_graph_replays(out_dtype):
+    """The NVFP4 linear (activation kernel + GEMM) with more 256 x 192 tiles (9 x 32) than
+    compute units, so each workgroup of the GEMM takes several tiles in turn (with a bf16
+    output, the next tile's first stage is copied during the current tile's last one),
+    captured in a graph: every replay bit-identical to the eager launch, with eager work
+    between the replays."""
+    M, K, N, r = 2100, 512, 6050, 32
+    print(f"nvfp4 graph replay M={M} K={K} N={N} out_dtype={out_dtype}", flush=True)
+    rng = np.random.default_rng(970 + out_dtype)
+    dev = "cuda:0"
+    x = gu.dev(synth.random_bf16(rng, (M, K), 1.0))
+    si = gu.dev(rng.uniform(0.5, 2.0, K).astype(np.float32))
+    l1 = gu.dev(synth.random_bf16(rng, (r, K), 0.05))
+    wc = gu.dev(synth.random_packed_nibbles(rng, N, K))
+    ws = gu.dev(rng.integers(0x30, 0x40, (N, K // 16)).astype(np.uint8))
+    l2 = gu.dev(synth.random_bf16(rng, (N, r), 0.1))
+    b = gu.dev(synth.random_bf16(rng, (N,), 0.3))
+    cfg = bd.LayerCfg.make(K, N, r, "nvfp4")
+    ac = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    asc = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    lora = torch.empty((M, r), dtype=torch.int16, device=dev)
+    out = torch.empty((M, N), dtype=torch.float32 if out_dtype == bd.SVDQ_DT_F32 else torch.int16, device=dev)
+    Sa, Sw = 0.01, 0.002
+
+    def step(stream):
+        sp = stream.cuda_stream
+        bd.svdq_quantize_act(cfg, M, x, si, l1, Sa, ac, asc, lora, sp)
+        bd.svdq_gemm_w4a4(cfg, M, ac, asc, Sa, wc, ws, Sw, lora, l2, b, bd.SVDQ_ACT_GELU_TANH, out_dtype,
+                          out, sp)
+
+    cur = torch.cuda.current_stream()
+    step(cur)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step(side)
+    torch.cuda.synchronize()
+    for k in range(3):
+        out.zero_()                        # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {k} differs from the eager launch"
+        step(cur)                          # and an eager step after it
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
