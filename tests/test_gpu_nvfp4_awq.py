@@ -114,14 +114,17 @@ def test_gemm_nvfp4_shapes(M, N, K, r, bias, act):
     gu.assert_bf16_close(yb, ref, cond, gu.nvfp4_nround(K, r), gelu=act == 1)
 
 
-def test_gemm_nvfp4_tiles_per_workgroup():
+@pytest.mark.parametrize("N", [6056, 6050])
+def test_gemm_nvfp4_tiles_per_workgroup(N):
     """More 256 x 192 tiles (9 x 32) than compute units, so a workgroup of the fast kernel
-    takes several tiles in turn (with a bf16 output, the next tile's first stage is copied
-    during the current tile's last one), with ragged last tile rows and columns; GELU,
-    bias and rank 32, both output types.  Sampled against the oracle: random points, every
-    column of the first, middle and last rows, every row of the first and last columns."""
-    M, N, K, r = 2100, 6050, 512, 32
-    rng = np.random.default_rng(77)
+    takes several tiles in turn, with ragged last tile rows and columns; GELU, bias and
+    rank 32, both output types.  N = 6056 (rows of whole 16-byte segments) stores through
+    LDS, and with a bf16 output copies the next tile's first stage during the current
+    tile's last one; N = 6050 stores element by element.  Sampled against the oracle:
+    random points, every column of the first, middle and last rows, every row of the first
+    and last columns."""
+    M, K, r = 2100, 512, 32
+    rng = np.random.default_rng(77 + N)
     ca, cw = synth.random_packed_nibbles(rng, M, K), synth.random_packed_nibbles(rng, N, K)
     sa = rng.integers(0, 0x7F, size=(M, K // 16)).astype(np.uint8)
     sw = rng.integers(0, 0x7F, size=(N, K // 16)).astype(np.uint8)
