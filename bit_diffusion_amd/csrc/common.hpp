@@ -35,11 +35,16 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 
 // GELU, tanh form: 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).  Evaluated as
 // the identical y / (1 + exp(-2u)), which keeps full relative accuracy for negative y where
-// 1 + tanh(u) would cancel.
+// 1 + tanh(u) would cancel, with the hardware's exp2 and reciprocal (about 1 ulp each):
+// e = 2^(-2 log2(e) u) and y * rcp(1 + e).  A relative error d in e moves the result by
+// at most e / (1 + e)^2 * d <= d / 4 of y, so the argument's rounding (|d| up to |x| ulp
+// for x = -2 log2(e) u) is damped where |x| is large; the result is within a few ulp of
+// |y|.  e overflows to inf for large negative y, whose reciprocal 0 gives the limit -0.
 __device__ __forceinline__ float gelu_tanh(float y) {
     const float c = 0.7978845608028654f;   // sqrt(2 / pi)
     const float u = c * (y + 0.044715f * y * y * y);
-    return y / (1.0f + expf(-2.0f * u));
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);   // -2 log2(e) u
+    return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 }  // namespace svdq
