@@ -171,11 +171,13 @@ def test_gemm_nvfp4_unaligned_scales():
 
 # M <= 4 with K a multiple of 512 up to 4096 runs the MFMA kernel, everything else the
 # reference kernel; N not a multiple of 16 leaves a partial column tile; N = 25000 at
-# K = 3072 needs more workgroups than fit in LDS at once (several columns runs per CU)
+# K = 3072 needs more workgroups than fit in LDS at once (several columns runs per CU);
+# N = 6 and 10 leave most of a workgroup's columns empty, K = 5120 is past the MFMA kernel
 @pytest.mark.parametrize("M,N,K", [
     (1, 64, 64), (2, 130, 3072), (5, 33, 512), (9, 100, 256), (3, 70, 768), (4, 96, 1024),
     (2, 64, 1536), (1, 40, 2048), (4, 50, 4096), (6, 50, 4096), (2, 32, 1152), (2, 48, 4160),
-    (13, 200, 3072), (1, 25000, 3072), (2, 1000, 512),
+    (13, 200, 3072), (1, 25000, 3072), (2, 1000, 512), (2, 6, 1024), (1, 100, 4096),
+    (2, 10, 5120), (2, 131, 3072),
 ])
 def test_awq_shapes(M, N, K):
     rng = np.random.default_rng(600 + M + N + K)
