@@ -197,9 +197,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     };
 
     const int fr = lane & 31, fh = lane >> 5;
-    // byte selectors of v_perm_b32 (bytes 0-3: the l word, 4-7: the h | m << 16 word)
-    const uint32_t psel0 = fh ? 0x07060100u : 0x05040504u;
-    const uint32_t psel1 = fh ? 0x01000706u : 0x05040706u;
 
     // The low-rank up-projection goes first: acc = lora_act . l2^T.  Its operand loads
     // (and the bias) are issued ahead of the first copies, so their latency hides behind
@@ -301,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
     // operands, three weight fragments and theirs.
     struct Frags {
         i32x8 a[2];
-        uint2 ax[2];   // the activation scale words, made into the MFMA operand by ap_of
+        uint2 ax[2];   // the activation scale words: the scale MFMA's A operand as stored
         i32x8 w[3];
         bf16x4 wp[3];
     };
@@ -329,13 +326,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
             f.wp[j] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(Bb + kFrag + lane * 8));
         }
     };
-    // The activation scale operand of the scale-product MFMA from the row's two words
-    // (h | m << 16, l): lanes 0-31 (h, h, m, h), lanes 32-63 (l, m, m, l).  Formed right
-    // before its MFMA, so the LDS read behind it has had time to land.
-    auto ap_of = [&](uint2 x) {
-        return __builtin_bit_cast(bf16x4, make_uint2(__builtin_amdgcn_perm(x.x, x.y, psel0),
-                                                     __builtin_amdgcn_perm(x.x, x.y, psel1)));
-    };
+    // The activation scale operand of the scale-product MFMA: the row's two words (h, h, m, l)
+    // serve both halves of the lanes as they are (packed_layout.hpp).
+    auto ap_of = [](uint2 x) { return __builtin_bit_cast(bf16x4, x); };
     // Software-pipelined: the two MFMAs of pair q+1 are issued around the fmas of pair q,
     // so the MFMA pipe and the VALU work at the same time within one wave.
     auto compute = [&](const Frags& f) {

@@ -11,12 +11,15 @@
 //   bytes [1024, 1536)  dwords 4-5 of lane L at 1024 + 8 L
 // followed by the operands of the bf16 scale MFMA (v_mfma_f32_32x32x8_bf16), which forms
 // the outer product sa[m] * w[n], w = 64 sw, from three-term bf16 splits
-// (h = bf16(s), m = bf16(s - h), l = bf16(s - h - m); h + m + l = s to ~2^-24):
-//   activations: per row (h | m << 16, l)                                   (256 bytes)
-//   weights:     per MFMA lane, lanes 0-31 (column L) (h | m << 16, h | l << 16),
-//                lanes 32-63 (column L - 32) (h | m << 16, l | m << 16)   (512 bytes)
-// With the activation lanes arranged as (ha, ha, ma, ha | la, ma, ma, la) the eight
-// products sum to (ha + ma + la)(hw + mw + lw) - la lw: the fp32 product to a few ulp.
+// (h = bf16(s), m = bf16(s - h), l = bf16(s - h - m); h + m + l = s to ~2^-27):
+//   activations: per row (h | h << 16, m | l << 16) = the bf16 values (h, h, m, l), read
+//                as they are by both halves of the MFMA's lanes               (256 bytes)
+//   weights:     per MFMA lane, lanes 0-31 (column L) (h | m << 16, h | h << 16) = (h, m, h, h),
+//                lanes 32-63 (column L - 32) (l, m | m << 16) = (l, 0, m, m)    (512 bytes)
+// so that the eight products (k = 0..3 from lanes 0-31, k = 4..7 from lanes 32-63) are
+// ha hw, ha mw, ma hw, la hw, ha lw, 0, ma mw, la mw and sum to
+// (ha + ma + la)(hw + mw + lw) - ma lw - la lw: the fp32 product to a few ulp (the two
+// dropped terms are below 2^-26 of it).
 //
 // Activation buffer:  [ceil(M / 256)][G][8 row blocks][1792 bytes]
 // Weight buffer:      [ceil(N / 192)][G][6 column blocks][2048 bytes]
@@ -69,18 +72,18 @@ __device__ __forceinline__ void split3(float s, uint32_t& h, uint32_t& m, uint32
     l = f32_to_bf16(r1 - __uint_as_float(m << 16));
 }
 
-// The activation scale pair of one row: (h | m << 16, l).
+// The activation scale pair of one row: (h | h << 16, m | l << 16).
 __device__ __forceinline__ uint2 act_scale_pair(float s) {
     uint32_t h, m, l;
     split3(s, h, m, l);
-    return make_uint2(h | (m << 16), l);
+    return make_uint2(h | (h << 16), m | (l << 16));
 }
 
 // The weight scale operand of MFMA lane L for w = 64 sw of its column.
 __device__ __forceinline__ uint2 wgt_scale_operand(float w, int L) {
     uint32_t h, m, l;
     split3(w, h, m, l);
-    return L < 32 ? make_uint2(h | (m << 16), h | (l << 16)) : make_uint2(h | (m << 16), l | (m << 16));
+    return L < 32 ? make_uint2(h | (m << 16), h | (h << 16)) : make_uint2(l, m | (m << 16));
 }
 
 }  // namespace packed

@@ -157,7 +157,7 @@ svdq_status awq_gemm_w4a16(int64_t M, int32_t K, int32_t N, int32_t group_size, 
  * Both operands are stored as exact FP6 (E2M3) values q/8 of the int4 codes in the lane
  * order of the gfx950 32x32x64 FP6 MFMA, 32 rows (or columns) x 64 channels per fragment,
  * each followed by the group scales as three-term bf16 splits (h = bf16(s), m = bf16(s - h),
- * l = bf16(s - h - m), h + m + l = s to ~2^-24) arranged as operands of a bf16 MFMA that
+ * l = bf16(s - h - m), h + m + l = s to ~2^-27) arranged as operands of a bf16 MFMA that
  * forms the scale products.  Activations take 6 bits per code plus 8 bytes per (row, group)
  * and are padded to a multiple of 256 rows; weights take 6 bits per code plus 16 bytes per
  * (column, group) and are padded to a multiple of 192 columns.  The buffers are opaque;

@@ -162,7 +162,7 @@ def _fp6_fields(dw):
 
 def decode_act_packed(buf, M, K):
     """Host-side reader of the packed activation layout (test infrastructure): returns the
-    int codes [Mp, K], the scale pairs (h | m << 16, l) [Mp, G, 2] and a flag that every
+    int codes [Mp, K], the scale pairs (h | h << 16, m | l << 16) [Mp, G, 2] and a flag that every
     field is canonical (no negative zero, magnitude <= 8)."""
     G = K // 64
     mb = (M + 255) // 256
@@ -180,8 +180,8 @@ def decode_act_packed(buf, M, K):
 
 
 def split_words(scales):
-    """The scale pair the packed layout stores per (row, group): (h | m << 16, l) with
-    h = bf16(s), m = bf16(s - h), l = bf16(s - h - m)."""
+    """The scale pair the packed layout stores per (row, group): (h | h << 16, m | l << 16)
+    with h = bf16(s), m = bf16(s - h), l = bf16(s - h - m)."""
     import synth
     s = np.asarray(scales, np.float32)
     h = synth.f32_to_bf16_bits(s).astype(np.uint32)
@@ -189,7 +189,7 @@ def split_words(scales):
     m = synth.f32_to_bf16_bits(r1).astype(np.uint32)
     r2 = (r1 - (m << 16).view(np.float32)).astype(np.float32)
     l = synth.f32_to_bf16_bits(r2).astype(np.uint32)
-    return np.stack([h | (m << 16), l], axis=-1)
+    return np.stack([h | (h << 16), m | (l << 16)], axis=-1)
 
 
 def awq(x_bf16, q, sc, z, bias=None, out_bf16=False):
@@ -229,8 +229,8 @@ def int4_nround(K, r):
     running sum (fma or add), plus the product errors, which add up to at most 8 units of
     the condition sum in total (nibble-operand kernel: scale product and product, 2 units;
     packed kernel: the eight-term scale-product MFMA, 7 units, and the three-term bf16
-    splits, 2^-2); r for the low-rank MFMA's sums; the bias, and the K split's fixed-order
-    sum of up to 8 parts."""
+    splits with the two cross terms the MFMA's operands leave out, under 2^-1); r for the
+    low-rank MFMA's sums; the bias, and the K split's fixed-order sum of up to 8 parts."""
     return 2 * (K // 64 + r + 8 + 1 + 8)
 
 
