@@ -32,6 +32,7 @@
 // at most a quarter of the GPU is split over K when the caller passes a workspace: each
 // split stores its partial tile there and a second kernel adds the splits in a fixed order.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -100,6 +101,20 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
 __device__ __forceinline__ void dma_chunk(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(uniform_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+// The same with the LDS address given as a wave-uniform base plus a constant, added straight
+// into M0 (one SALU instruction instead of an add and a move).
+template <uint32_t kOff>
+__device__ __forceinline__ void dma_chunk_at(const uint8_t* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(uniform_ptr(sbase)), "s"(lds_base), "n"(kOff) : "memory", "scc");
+}
+template <uint32_t kOff>
+__device__ __forceinline__ void dma_chunk_at_m(const uint8_t* sbase, uint32_t voff, uint32_t lds_base, uint64_t mask) {
+    uint64_t saved;
+    asm volatile("s_add_u32 m0, %2, %5\n\ts_and_saveexec_b64 %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(lds_base), "s"(uniform_u64(mask)), "s"(uniform_ptr(sbase)), "n"(kOff)
+                 : "memory", "scc");
 }
 // The same under exec & mask (mask 0 or all ones, wave-uniform): with mask 0 no lane
 // accesses memory.  Code that waits on these counts them as if they were issued, which is
@@ -252,12 +267,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         src0[j] = uniform_u64((uint64_t)chunk_src(0, c));
         step[j] = __builtin_amdgcn_readfirstlane(cg < kAChunks ? 2 * kAStage : 2 * kBStage);
     }
-    auto issue_j = [&](int t, int j) {   // groups 2t and 2t + 1 both exist
-        const int c = wave + 8 * j;
-        const uint32_t dst = lds0 + (t % 3) * (2 * kStageBytes) + c * 1024;
+    // Copy j of third t: chunk wave + 8 j, at LDS offset base_t + 8 KiB j, base_t the third's
+    // buffer plus this wave's first chunk (computed once per third, in an SGPR).
+    auto issue_j = [&](int t, auto jc, uint32_t base_t) {   // groups 2t and 2t + 1 both exist
+        constexpr int j = decltype(jc)::value;
         const uint8_t* src = (const uint8_t*)(src0[j] + (uint64_t)((uint32_t)t * step[j]));
-        if (j < 6) dma_chunk(src, voff, dst);
-        else dma_chunk_m(src, voff, dst, mask_lo4);
+        if constexpr (j < 6) dma_chunk_at<8192u * j>(src, voff, base_t);
+        else dma_chunk_at_m<8192u * j>(src, voff, base_t, mask_lo4);
     };
     for (int h = 0; h < min(G, 4); ++h) issue(h, h);
 
@@ -410,13 +426,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
             load_frags(S, f);
             // third t+2's copies go into third t-1's buffer, which the barrier above
             // released, early in the third so they have two thirds to land
+            const uint32_t base_t = __builtin_amdgcn_readfirstlane(lds0 + ((t + 2) % 3) * (2 * kStageBytes) + wave * 1024);
             compute2(f, f1, S + kStageBytes, [&](int q) {
+                using std::integral_constant;
                 if (q == 0) {
-#pragma unroll
-                    for (int j = 0; j < 3; ++j) issue_j(t + 2, j);
+                    issue_j(t + 2, integral_constant<int, 0>{}, base_t);
+                    issue_j(t + 2, integral_constant<int, 1>{}, base_t);
+                    issue_j(t + 2, integral_constant<int, 2>{}, base_t);
                 } else {
-#pragma unroll
-                    for (int j = 3; j < 7; ++j) issue_j(t + 2, j);
+                    issue_j(t + 2, integral_constant<int, 3>{}, base_t);
+                    issue_j(t + 2, integral_constant<int, 4>{}, base_t);
+                    issue_j(t + 2, integral_constant<int, 5>{}, base_t);
+                    issue_j(t + 2, integral_constant<int, 6>{}, base_t);
                 }
             });
             __builtin_amdgcn_sched_barrier(0);
