@@ -416,17 +416,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
         }
     };
 
+    // byte offsets of the buffers of thirds t and t + 2, rotated over the three buffers
+    constexpr uint32_t kBuf = 2 * kStageBytes;
+    uint32_t off_t = 0, off_t2 = 2 * kBuf;
+    const uint32_t lds_w = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
     int t = 0;
     for (; 2 * t + 5 < G; ++t) {   // the third two ahead (groups 2t+4, 2t+5) exists
         wait_vm<6>();   // this wave's copies of third t have landed (third t+1's may not)
         barrier();      // every wave's have; third t-1's buffer is no longer read
-        const uint8_t* S = smem + (t % 3) * (2 * kStageBytes);
+        const uint8_t* S = smem + off_t;
         {
             Frags f, f1;
             load_frags(S, f);
             // third t+2's copies go into third t-1's buffer, which the barrier above
             // released, early in the third so they have two thirds to land
-            const uint32_t base_t = __builtin_amdgcn_readfirstlane(lds0 + ((t + 2) % 3) * (2 * kStageBytes) + wave * 1024);
+            const uint32_t base_t = lds_w + off_t2;
             compute2(f, f1, S + kStageBytes, [&](int q) {
                 using std::integral_constant;
                 if (q == 0) {
@@ -442,6 +446,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_w4a4_fp6_kernel(PackedGemmAr
             });
             __builtin_amdgcn_sched_barrier(0);
         }
+        off_t = off_t == 2 * kBuf ? 0u : off_t + kBuf;
+        off_t2 = off_t2 == 2 * kBuf ? 0u : off_t2 + kBuf;
     }
     // tail: thirds t and t+1 are issued; at most one group (2t+4 = G-1) is not
     wait_vm<0>();
