@@ -201,6 +201,18 @@ __device__ __forceinline__ void fdma_x4(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(g), "s"(lds) : "memory");
 }
+// The same from a wave-uniform base (SGPRs) plus the lane's 32-bit byte offset, so that a
+// stage's advance is one scalar add instead of a 64-bit vector add per copy.
+__device__ __forceinline__ void fdma_x4_s(const uint8_t* base, uint32_t voff, uint32_t lds) {
+    // readfirstlane returns a signed int: each half goes through uint32_t so that the low
+    // half is zero-extended (sign-extended, it would set the high half when bit 31 is set)
+    const uint64_t v = (uint64_t)base;
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint64_t b = ((uint64_t)hi << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"((const uint8_t*)b), "s"(lds) : "memory");
+}
 __device__ __forceinline__ void fdma_x1(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :: "v"(g), "s"(lds) : "memory");
@@ -322,25 +334,29 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
     // chunk c = (l % 8) ^ ((row / 2) % 8), which is the same for every j of the wave.
     const int lrow = lane >> 3;
     const int c16 = 16 * ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
-    // first source byte of each of the wave's copies for a tile (stage 0)
-    auto tile_src = [&](int64_t m0, int n0, const uint8_t* (&src)[8]) {
+    // byte offset of each of the wave's copies for a tile (stage 0), from the start of the
+    // array it reads (codes of A, codes of W, scales of A for waves 0-3 or of W for 4-6)
+    auto tile_off = [&](int64_t m0, int n0, uint32_t (&off)[8]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            src[q] = acodes + min(m0 + 8 * (wave + 8 * q) + lrow, M - 1) * (K / 2) + c16;
+            off[q] = (uint32_t)(min(m0 + 8 * (wave + 8 * q) + lrow, M - 1) * (K / 2) + c16);
 #pragma unroll
         for (int q = 0; q < 3; ++q)
-            src[4 + q] = wcodes + (int64_t)min(n0 + 8 * (wave + 8 * q) + lrow, N - 1) * (K / 2) + c16;
-        src[7] = wave < 4 ? ascales + min(m0 + 64 * wave + lane, M - 1) * (K / 16)
-                          : wscales + (int64_t)min(n0 + 64 * (wave - 4) + lane, N - 1) * (K / 16);
+            off[4 + q] = (uint32_t)((int64_t)min(n0 + 8 * (wave + 8 * q) + lrow, N - 1) * (K / 2) + c16);
+        off[7] = wave < 4 ? (uint32_t)(min(m0 + 64 * wave + lane, M - 1) * (K / 16))
+                          : (uint32_t)((int64_t)min(n0 + 64 * (wave - 4) + lane, N - 1) * (K / 16));
     };
+    const uint8_t* sbase = wave < 4 ? ascales : wscales;   // this wave's scale copies
     // the copies of the stage starting at channel kc into buffer b
-    auto issue = [&](const uint8_t* const (&src)[8], int kc, int b) {
+    auto issue = [&](const uint32_t (&off)[8], int kc, int b) {
         const uint32_t base = lds0 + b * kFStage;
+        const uint8_t* ab = acodes + kc / 2;
+        const uint8_t* wb = wcodes + kc / 2;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) fdma_x4(src[q] + kc / 2, base + 1024 * (wave + 8 * q));
+        for (int q = 0; q < 4; ++q) fdma_x4_s(ab, off[q], base + 1024 * (wave + 8 * q));
 #pragma unroll
-        for (int q = 0; q < 3; ++q) fdma_x4(src[4 + q] + kc / 2, base + kCA + 1024 * (wave + 8 * q));
-        if (wave < 7) fdma_x4(src[7] + kc / 16, base + kCA + kCB + 1024 * wave);
+        for (int q = 0; q < 3; ++q) fdma_x4_s(wb, off[4 + q], base + kCA + 1024 * (wave + 8 * q));
+        if (wave < 7) fdma_x4_s(sbase + kc / 16, off[7], base + kCA + kCB + 1024 * wave);
     };
 
     // ---- compute one 64-channel sub-stage u of stage buffer b.  The MFMA contracts any
@@ -412,8 +428,8 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-        const uint8_t* src[8];
-        tile_src(m0, n0, src);
+        uint32_t src[8];
+        tile_off(m0, n0, src);
         if (!ahead) {
             if (tile != blockIdx.x) fbarrier();   // every wave is done with the last epilogue's LDS
             issue(src, 0, gs & 1);
@@ -432,8 +448,8 @@ __global__ __launch_bounds__(kFThreads, 1) void gemm_nvfp4_f16_kernel(GemmArgs p
                 int64_t cm0 = nm0;
                 int cn0 = nn0;
                 asm volatile("" : "+s"(cm0), "+s"(cn0));   // keeps these addresses out of the loop
-                const uint8_t* nsrc[8];
-                tile_src(cm0, cn0, nsrc);
+                uint32_t nsrc[8];
+                tile_off(cm0, cn0, nsrc);
                 issue(nsrc, 0, (gs + S) & 1);
             }
 #pragma unroll
@@ -563,7 +579,9 @@ void launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) {
                       (reinterpret_cast<uintptr_t>(a.wscales) % 16) == 0;
     const int64_t num_m = (a.M + kFM - 1) / kFM;
     const int num_n = (a.N + kFN - 1) / kFN;
-    if (fast && num_m * num_n < ((int64_t)1 << 31) && gemm_nvfp4_init()) {
+    // the copies address rows by 32-bit byte offsets from the start of each array
+    const bool small = a.M * (a.K / 2) < ((int64_t)1 << 31) && (int64_t)a.N * (a.K / 2) < ((int64_t)1 << 31);
+    if (fast && small && num_m * num_n < ((int64_t)1 << 31) && gemm_nvfp4_init()) {
         // one workgroup per CU (the LDS of two stage buffers allows no more), each taking
         // every grid-th tile; a multiple of 8 keeps each XCD on its own range of tiles
         const int64_t nt = num_m * num_n;
