@@ -109,20 +109,15 @@ __device__ __forceinline__ void dma_chunk_at(const uint8_t* sbase, uint32_t voff
     asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(uniform_ptr(sbase)), "s"(lds_base), "n"(kOff) : "memory", "scc");
 }
+// The same under exec & mask (mask 0 or all ones, wave-uniform): with mask 0 no lane
+// accesses memory.  Code that waits on these counts them as if they were issued, which is
+// exact or one copy too strict either way.
 template <uint32_t kOff>
 __device__ __forceinline__ void dma_chunk_at_m(const uint8_t* sbase, uint32_t voff, uint32_t lds_base, uint64_t mask) {
     uint64_t saved;
     asm volatile("s_add_u32 m0, %2, %5\n\ts_and_saveexec_b64 %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\ts_mov_b64 exec, %0"
                  : "=&s"(saved) : "v"(voff), "s"(lds_base), "s"(uniform_u64(mask)), "s"(uniform_ptr(sbase)), "n"(kOff)
                  : "memory", "scc");
-}
-// The same under exec & mask (mask 0 or all ones, wave-uniform): with mask 0 no lane
-// accesses memory.  Code that waits on these counts them as if they were issued, which is
-// exact or one copy too strict either way.
-__device__ __forceinline__ void dma_chunk_m(const uint8_t* sbase, uint32_t voff, uint32_t lds, uint64_t mask) {
-    uint64_t saved;
-    asm volatile("s_mov_b32 m0, %2\n\ts_and_saveexec_b64 %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\ts_mov_b64 exec, %0"
-                 : "=&s"(saved) : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(uniform_u64(mask)), "s"(uniform_ptr(sbase)) : "memory", "scc");
 }
 
 // Output tile t (row-major over groups of four tile rows) -> tile coordinates.

@@ -194,15 +194,11 @@ __device__ __forceinline__ void fbarrier() {
 
 typedef __attribute__((address_space(3))) uint8_t flds_u8;
 
-// Global -> LDS copies (LDS DMA): lane l moves 16 (x4) or 4 (dword) bytes from its own
-// global address to LDS byte lds + 16 l (+ 4 l).  The s_nop is the wait state an LDS DMA
-// needs after an SALU write of M0.  Completion: s_waitcnt vmcnt(0) before the barrier.
-__device__ __forceinline__ void fdma_x4(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds) : "memory");
-}
-// The same from a wave-uniform base (SGPRs) plus the lane's 32-bit byte offset, so that a
-// stage's advance is one scalar add instead of a 64-bit vector add per copy.
+// Global -> LDS copy (LDS DMA): lane l moves the 16 bytes at base + voff (base wave-uniform,
+// in SGPRs; voff the lane's 32-bit byte offset) to LDS byte lds + 16 l, so that a stage's
+// advance is one scalar add instead of a 64-bit vector add per copy.  The s_nop is the wait
+// state an LDS DMA needs after an SALU write of M0.  Completion: s_waitcnt vmcnt(0) before
+// the barrier.
 __device__ __forceinline__ void fdma_x4_s(const uint8_t* base, uint32_t voff, uint32_t lds) {
     // readfirstlane returns a signed int: each half goes through uint32_t so that the low
     // half is zero-extended (sign-extended, it would set the high half when bit 31 is set)
@@ -212,10 +208,6 @@ __device__ __forceinline__ void fdma_x4_s(const uint8_t* base, uint32_t voff, ui
     const uint64_t b = ((uint64_t)hi << 32) | lo;
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"((const uint8_t*)b), "s"(lds) : "memory");
-}
-__device__ __forceinline__ void fdma_x1(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(g), "s"(lds) : "memory");
 }
 
 // 8 codes (a dword, code 2i in the low nibble of byte i) times the E4M3 scale sc as an
