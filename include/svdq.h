@@ -123,7 +123,7 @@ svdq_status svdq_quantize_act(const svdq_layer_cfg* cfg, int64_t M, const void* 
  * For INT4 this call is the reference path on the plain nibble format: it contracts the
  * nibbles on the int8 MFMA with 128x128 tiles (about 151 us at M = 4096, K = N = 3072 on
  * an MI355X).  The primary INT4 path is the packed one below (svdq_prepack_weight once per
- * layer, svdq_quantize_act_packed, svdq_gemm_w4a4_packed: about 46 us for that GEMM), with
+ * layer, svdq_quantize_act_packed, svdq_gemm_w4a4_packed: about 42 us for that GEMM), with
  * the same result up to fp32 rounding order.
  */
 svdq_status svdq_gemm_w4a4(const svdq_layer_cfg* cfg, int64_t M, const void* act_codes,
