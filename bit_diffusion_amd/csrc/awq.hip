@@ -15,9 +15,9 @@
 //
 // Fast kernel (M <= 4, K a multiple of 512 up to 4096): one workgroup per CU, each owning
 // an equal run of output columns (weight rows), so every CU streams the same number of
-// bytes.  At start every wave copies its share of x, the scales and zeros, and its K slice
-// (4 groups = 128 bytes of every weight row of the run) into LDS with global_load_lds_dwordx4
-// -- a whole run is in flight at once, and every copy instruction reads 8 rows x 128
+// bytes.  Every wave copies its share of x, the scales and zeros, and its K slice (4 groups
+// = 128 bytes of every weight row of the run) into LDS with global_load_lds_dwordx4, two
+// half tiles of codes ahead of the tile it computes; every code copy reads 8 rows x 128
 // contiguous bytes.  Within each 8-row x 128-byte block the 16-byte chunks are stored
 // XOR-swizzled by row, so that the MFMA-operand reads below are free of bank conflicts.
 // Wave w then runs v_mfma_f32_16x16x32_bf16 over its slice, 16 columns at a time, as soon
@@ -69,8 +69,7 @@ __device__ __forceinline__ void awq_dma(const void* gaddr, uint32_t lds) {
 //          workgroup's columns (<= 128 bf16); the scale reads of a partial last tile (at
 //          most 240 B past the copied pieces) may land there
 // Everything a wave reads is copied by that wave, so waves run without barriers until the
-// slices are added; each keeps kAwqAhead half tiles of copies in flight (more would make it
-// block in issue once the CU's queue of copies is full).
+// slices are added; each keeps kAwqAhead half tiles of codes in flight (below).
 struct AwqRegion {
     int halves, xkb, sbytes;
     __host__ __device__ AwqRegion(int64_t M, int cols)
@@ -82,7 +81,12 @@ __host__ inline size_t awq_lds_bytes(int64_t M, int K, int cols) {
     return (size_t)(K / 64 / kAwqSliceGroups) * AwqRegion(M, cols).bytes();
 }
 
-constexpr int kAwqAhead = 4;
+// Half tiles of codes in flight per wave: a tile reads two, so at least 2; the tile after
+// the current one goes out as soon as the current tile's codes are in registers.  Fewer in
+// flight per wave measured faster (9.3 us at 2, 9.5 at 3, 9.7 at 4 on the modulation
+// layer, M = 2, K = 3072, N = 18432); the twelve waves of a CU still keep ~24 in flight.
+constexpr int kAwqAhead = 2;
+static_assert(kAwqAhead >= 2, "a tile reads two half tiles");
 
 __device__ __forceinline__ void awq_wait_vm_rt(int n) {   // n in [0, 16]
     switch (n) {
